@@ -1,0 +1,265 @@
+"""Benchmark of the scaled FP8 GEMM hot path on one MI355X.
+
+One step = the whole per-tensor path on FP32 inputs already resident in HBM:
+amax + scale + E4M3 quantization of A and of B, then the FP8 GEMM with FP32
+accumulation and the fused scale/BF16 epilogue.  The default workload is the
+M = N = K = 8192 GEMM with BF16 output (A, B drawn N(0, 1) from a seed).
+
+Printed (rank 0, one JSON line):
+  value       -- whole-step throughput, 2*M*N*K flops per step / step time
+                 (TFLOP/s; quantization time included)
+  gemm_tflops -- the GEMM kernel alone: 2*M*N*K / its average launch time,
+                 measured with HIP events on the launch stream
+  roofline    -- that GEMM kernel against the dense FP8 MFMA peak
+  cpu_baseline-- the CPU oracle timed on a bounded sample of the same step
+Other workloads (--workload) serve profiling of the other shape classes.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (published; 256 CU x 8192 flop/clk x 2.4 GHz = 5033)
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gemm8192",
+                    choices=["gemm8192", "gemm1024", "gemm256", "llm16", "llm128", "llm4096", "blockscaled8192",
+                             "moe"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=768, help="rows of A in the oracle's timed sample")
+    return ap.parse_args()
+
+
+class Workload:
+    """Inputs resident on the GPU and one step of the hot path."""
+
+    def __init__(self, name, dev):
+        import torch
+        import precision_dense_linear_amd as P
+        from precision_dense_linear_amd import workloads as W
+        self.P, self.torch, self.name = P, torch, name
+        g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        self.kind = "pertensor"
+        self.out = torch.bfloat16
+        if name.startswith("gemm"):
+            n = int(name[4:])
+            self.M = self.N = self.K = n
+            a, b = W.pertensor_pair(n, n, n, seed=0)
+            self.desc = "per-tensor FP8 GEMM M=N=K=%d, BF16 out; A, B FP32 N(0,1) quantized to e4m3fn on device" % n
+            if n == 256:
+                self.out = torch.float32
+                self.desc = self.desc.replace("BF16", "FP32")
+        elif name.startswith("llm"):
+            self.M = int(name[3:])
+            self.N = 8192 if self.M == 16 else 28672
+            self.K = 8192
+            a, b = W.llm_linear(self.M, self.N, self.K)
+            self.desc = ("LLM linear layer M=%d N=%d K=%d, per-tensor FP8, BF16 out; activations N(0,1) with 1%% "
+                         "outlier channels x20, weights N(0,0.02)" % (self.M, self.N, self.K))
+        elif name == "blockscaled8192":
+            self.kind = "block"
+            self.M = self.N = self.K = 8192
+            a, b = W.blockscaled_pair(8192, 8192, 8192)
+            self.desc = "block-scaled (32x32 tiles) FP8 GEMM M=N=K=8192, BF16 out; tile factors 10^U(-2,2)"
+        else:
+            self.kind = "moe"
+            x, w, off = W.moe()
+            self.E, self.K, self.N = w.shape
+            self.M = x.shape[0]
+            a, b = x, w.reshape(self.E * self.K, self.N)
+            self.off = g(off.astype(np.int32))
+            self.woff = g((np.arange(self.E + 1) * self.K).astype(np.int32))
+            self.desc = ("MoE grouped FP8 GEMM: 8 experts, 16384 tokens with Zipf(1.2) counts %s, K=4096, N=14336, "
+                         "BF16 out" % list(np.diff(off)))
+        self.a_host, self.b_host = a, b
+        self.A, self.B = g(a), g(b)
+        self.qa = torch.empty(a.shape, dtype=torch.uint8, device=dev)
+        self.qb = torch.empty(b.shape, dtype=torch.uint8, device=dev)
+        self.C = torch.empty((self.M, self.N), dtype=self.out, device=dev)
+        if self.kind == "pertensor":
+            self.sa, self.aa = (torch.empty(1, device=dev) for _ in range(2))
+            self.sb, self.ab = (torch.empty(1, device=dev) for _ in range(2))
+        elif self.kind == "block":
+            self.sa = torch.empty((self.M // 32, self.K // 32), device=dev)
+            self.sb = torch.empty((self.K // 32, self.N // 32), device=dev)
+        else:
+            self.sa, self.aa = (torch.empty(self.E, device=dev) for _ in range(2))
+            self.sb, self.ab = (torch.empty(self.E, device=dev) for _ in range(2))
+        self.flops = 2.0 * self.M * self.N * self.K
+
+    def quantize(self):
+        P = self.P
+        if self.kind == "pertensor":
+            P.fp8_quantize(self.A, self.qa, self.sa, self.aa)
+            P.fp8_quantize(self.B, self.qb, self.sb, self.ab)
+        elif self.kind == "block":
+            P.fp8_quantize_blocked(self.A, self.qa, self.sa)
+            P.fp8_quantize_blocked(self.B, self.qb, self.sb)
+        else:
+            P.fp8_quantize_grouped(self.A, self.off, self.qa, self.sa, self.aa)
+            P.fp8_quantize_grouped(self.B, self.woff, self.qb, self.sb, self.ab)
+
+    def gemm(self, fast=False):
+        P = self.P
+        if self.kind == "pertensor":
+            P.fp8_gemm(self.qa, self.qb, self.sa, self.sb, self.out, C=self.C, fast=fast)
+        elif self.kind == "block":
+            P.fp8_gemm_blockscaled(self.qa, self.qb, self.sa, self.sb, self.out, C=self.C)
+        else:
+            P.fp8_grouped_gemm(self.qa, self.qb.view(self.E, self.K, self.N), self.off, self.sa, self.sb, self.out,
+                               C=self.C, fast=fast)
+
+    def step(self):
+        self.quantize()
+        self.gemm()
+
+    def gemm_bytes(self):
+        """Algorithmic HBM bytes of one GEMM launch: A and B codes once, C once."""
+        osz = 2 if self.out == self.torch.bfloat16 else 4
+        if self.kind == "moe":
+            return self.M * self.K + self.E * self.K * self.N + self.M * self.N * osz
+        extra = (self.M // 32) * (self.K // 32) * 4 + (self.K // 32) * (self.N // 32) * 4 if self.kind == "block" else 0
+        return self.M * self.K + self.K * self.N + self.M * self.N * osz + extra
+
+
+def cpu_baseline(w: Workload, rows: int):
+    """The oracle on a bounded sample of the step: quantize B fully and `rows`
+    rows of A, GEMM those rows; extrapolated to a full step."""
+    import oracle
+    M = w.M
+    r = min(rows, M)
+    sel = np.arange(r)
+    t0 = time.perf_counter()
+    if w.kind == "pertensor":
+        qa, sa, _ = oracle.quantize_pertensor(w.a_host[:r])
+        tqa = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        qb, sb, _ = oracle.quantize_pertensor(w.b_host)
+        tqb = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.gemm_rows(qa, qb, sa, sb, oracle.BF16 if w.out != w.torch.float32 else oracle.F32, rows=sel)
+        tg = time.perf_counter() - t0
+    else:
+        return None
+    t_step = tqa * M / r + tqb + tg * M / r
+    return {"value": round(w.flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "quantize %d of %d rows of A (%.2fs) and all of B (%.2fs), exact FP64 GEMM of those %d rows "
+                      "(%.2fs); scaled to one full step = %.1fs" % (r, M, tqa, tqb, r, tg, t_step)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = Workload(args.workload, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+
+    # Timed region: K whole steps; GEMM launches bracketed by events on the
+    # same stream to get the kernel's own average duration.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        w.quantize()
+        ev[i][0].record(stream)
+        w.gemm()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gemm_ms = [s.elapsed_time(e) for s, e in ev]
+
+    # the native-FP8-accumulation GEMM (FP8_ACC_FAST), timed the same way, outside the timed region
+    fast = None
+    if w.kind != "block":
+        for _ in range(3):
+            w.gemm(fast=True)
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for s_, e_ in fev:
+            s_.record(stream)
+            w.gemm(fast=True)
+            e_.record(stream)
+        torch.cuda.synchronize()
+        fms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in fev]))
+        ft = w.flops / (fms * 1e-3) / 1e12
+        fast = {"gemm_tflops": round(ft, 2), "pct_fp8_peak": round(100 * ft / FP8_PEAK_TFLOPS, 2),
+                "avg_kernel_us": round(fms * 1e3, 2)}
+
+    # quantize alone (for the GB/s figure), outside the timed region
+    qev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    qev[0].record(stream)
+    for _ in range(5):
+        w.quantize()
+    qev[1].record(stream)
+    torch.cuda.synchronize()
+    q_ms = qev[0].elapsed_time(qev[1]) / 5
+    q_bytes = w.A.numel() * 5 + w.B.numel() * 5 + w.A.numel() * 4 + w.B.numel() * 4  # amax read; read + code write
+
+    ms_step = elapsed * 1e3 / args.steps
+    avg_gemm_ms = float(np.mean(gemm_ms))
+    gemm_tflops = w.flops / (avg_gemm_ms * 1e-3) / 1e12
+    mfma_bound = w.flops / w.gemm_bytes() > FP8_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        gbps = w.gemm_bytes() / (avg_gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+    roof["kernel"] = "gemm_kernel (fp8_gemm)" if w.kind == "pertensor" else (
+        "gemm_blockscaled_kernel" if w.kind == "block" else "gemm_kernel (fp8_grouped_gemm)")
+    roof["avg_kernel_us"] = round(avg_gemm_ms * 1e3, 2)
+
+    out = {
+        "metric": "FP8 GEMM TFLOPS at M=N=K=8192 (BF16 out) + % of MI355X dense FP8 peak",
+        "value": round(w.flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": w.desc, "M": w.M, "N": w.N, "K": w.K,
+                   "out": "bf16" if w.out == torch.bfloat16 else "f32", "step": "quantize A and B + GEMM"},
+        "gemm_tflops": round(gemm_tflops, 2),
+        "gemm_pct_fp8_peak": round(100 * gemm_tflops / FP8_PEAK_TFLOPS, 2),
+        "quantize_ms": round(q_ms, 4),
+        "quantize_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+        "roofline": roof,
+        "fp8_acc_fast": fast,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

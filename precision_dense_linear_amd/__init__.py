@@ -1,0 +1,202 @@
+"""MI355X (gfx950) scaled FP8 GEMM: thin Python binding over libfp8gemm.so.
+
+Every function here only marshals arguments: it takes torch tensors on a
+ROCm device, allocates missing outputs with torch (device memory is the only
+thing torch provides), and calls the C ABI of include/fp8gemm.h with raw
+device pointers and torch's current HIP stream.  All arithmetic runs in the
+library's HIP kernels; if the library is missing the import fails.
+
+Entry points (same names as the C ABI):
+    fp8_quantize(x)                          -> (q, scale, amax)
+    fp8_quantize_blocked(x)                  -> (q, tile_scales)
+    fp8_quantize_grouped(x, offsets)         -> (q, scales, amax)
+    fp8_gemm(A, B, scale_a, scale_b, out_dtype)
+    fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype)
+    fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype)
+E4M3 codes are passed as torch.uint8 or torch.float8_e4m3fn tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8gemm.so")
+
+FP8_OK, FP8_ERR_INVALID_ARG, FP8_ERR_UNSUPPORTED_SHAPE, FP8_ERR_HIP = 0, 1, 2, 3
+FP8_OUT_F32, FP8_OUT_BF16 = 0, 1
+FP8_ACC_FAST = 0x100  # native FP8 matrix-core accumulation (see include/fp8gemm.h)
+
+SYMBOLS = ("fp8_quantize", "fp8_quantize_blocked", "fp8_quantize_grouped", "fp8_gemm",
+           "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_status_string", "fp8_last_error")
+
+
+class FP8Error(RuntimeError):
+    def __init__(self, func: str, status: int, message: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (func, status_name(status), message))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libfp8gemm.so is not built (%s); run __graft_entry__.build() or "
+                          "python -m precision_dense_linear_amd._build" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    st = ctypes.c_int
+    L.fp8_quantize.argtypes = [P, i64, P, P, P, P]
+    L.fp8_quantize_blocked.argtypes = [P, i64, i64, P, P, P]
+    L.fp8_quantize_grouped.argtypes = [P, i64, i64, P, i32, P, P, P, P]
+    L.fp8_gemm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
+    L.fp8_gemm_blockscaled.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
+    L.fp8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i64, i64, i64, i32, P]
+    for f in ("fp8_quantize", "fp8_quantize_blocked", "fp8_quantize_grouped", "fp8_gemm",
+              "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
+        getattr(L, f).restype = st
+    L.fp8_status_string.restype = ctypes.c_char_p
+    L.fp8_status_string.argtypes = [i32]
+    L.fp8_last_error.restype = ctypes.c_char_p
+    L.fp8_last_error.argtypes = []
+    return L
+
+
+lib = _load()
+
+
+def status_name(status: int) -> str:
+    return lib.fp8_status_string(status).decode()
+
+
+def _check(func: str, status: int):
+    if status != FP8_OK:
+        raise FP8Error(func, status, lib.fp8_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _codes(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError("E4M3 operands must be torch.uint8 or torch.float8_e4m3fn, got %s" % t.dtype)
+    return t
+
+
+def _stream(dev: torch.device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _out_code(out_dtype) -> int:
+    if out_dtype in (torch.float32, "f32", "fp32", FP8_OUT_F32):
+        return FP8_OUT_F32
+    if out_dtype in (torch.bfloat16, "bf16", FP8_OUT_BF16):
+        return FP8_OUT_BF16
+    raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def fp8_quantize(x: torch.Tensor, q=None, scale=None, amax=None, stream=None):
+    """Per-tensor E4M3 quantization; returns (q uint8, scale float32[1], amax float32[1])."""
+    _require(x.is_cuda and x.dtype == torch.float32 and x.is_contiguous(), "x must be a contiguous float32 GPU tensor")
+    dev = x.device
+    q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else q
+    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
+    amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else amax
+    with torch.cuda.device(dev):
+        _check("fp8_quantize", lib.fp8_quantize(_ptr(x), x.numel(), _ptr(q), _ptr(scale), _ptr(amax),
+                                                _stream(dev, stream)))
+    return q, scale, amax
+
+
+def fp8_quantize_blocked(x: torch.Tensor, q=None, tile_scales=None, stream=None):
+    """32x32-tile E4M3 quantization of a 2-D tensor; returns (q, tile_scales[rows/32, cols/32])."""
+    _require(x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 2,
+             "x must be a contiguous 2-D float32 GPU tensor")
+    rows, cols = x.shape
+    dev = x.device
+    q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else q
+    if tile_scales is None:
+        tile_scales = torch.empty((rows // 32, cols // 32), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check("fp8_quantize_blocked", lib.fp8_quantize_blocked(_ptr(x), rows, cols, _ptr(q), _ptr(tile_scales),
+                                                                _stream(dev, stream)))
+    return q, tile_scales
+
+
+def fp8_quantize_grouped(x: torch.Tensor, offsets: torch.Tensor, q=None, scales=None, amax=None, stream=None):
+    """Row-group E4M3 quantization (group g = rows offsets[g]..offsets[g+1]); returns (q, scales, amax)."""
+    _require(x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 2,
+             "x must be a contiguous 2-D float32 GPU tensor")
+    _require(offsets.is_cuda and offsets.dtype == torch.int32, "offsets must be an int32 GPU tensor")
+    rows, cols = x.shape
+    G = offsets.numel() - 1
+    dev = x.device
+    q = torch.zeros(x.shape, dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty(G, dtype=torch.float32, device=dev) if scales is None else scales
+    amax = torch.empty(G, dtype=torch.float32, device=dev) if amax is None else amax
+    with torch.cuda.device(dev):
+        _check("fp8_quantize_grouped", lib.fp8_quantize_grouped(_ptr(x), rows, cols, _ptr(offsets), G, _ptr(q),
+                                                                _ptr(scales), _ptr(amax), _stream(dev, stream)))
+    return q, scales, amax
+
+
+def _out_tensor(C, shape, code, dev):
+    if C is not None:
+        return C
+    return torch.empty(shape, dtype=torch.float32 if code == FP8_OUT_F32 else torch.bfloat16, device=dev)
+
+
+def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=None, fast=False):
+    """C = scale_a*scale_b * A @ B with E4M3 A (M x K) and B (K x N), FP32 accumulation.
+
+    fast=True selects the native FP8 matrix-core accumulation (FP8_ACC_FAST)."""
+    A, B = _codes(A), _codes(B)
+    M, K = A.shape
+    N = B.shape[1]
+    _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
+    code = _out_code(out_dtype)
+    C = _out_tensor(C, (M, N), code, A.device)
+    with torch.cuda.device(A.device):
+        _check("fp8_gemm", lib.fp8_gemm(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N, K,
+                                        code | (FP8_ACC_FAST if fast else 0), _stream(A.device, stream)))
+    return C
+
+
+def fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype=torch.bfloat16, C=None, stream=None):
+    """C = sum over 32-wide K blocks of s_a*s_b * (A_kb @ B_kb), 32x32 tile scales."""
+    A, B = _codes(A), _codes(B)
+    M, K = A.shape
+    N = B.shape[1]
+    _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
+    code = _out_code(out_dtype)
+    C = _out_tensor(C, (M, N), code, A.device)
+    with torch.cuda.device(A.device):
+        _check("fp8_gemm_blockscaled", lib.fp8_gemm_blockscaled(_ptr(A), _ptr(B), _ptr(s_a), _ptr(s_b), _ptr(C),
+                                                                M, N, K, code, _stream(A.device, stream)))
+    return C
+
+
+def fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=None, fast=False):
+    """MoE grouped GEMM: rows offsets[e]..offsets[e+1] of A times B[e], scaled by scale_a[e]*scale_b[e]."""
+    A, B = _codes(A), _codes(B)
+    T, K = A.shape
+    E, K2, N = B.shape
+    _require(K2 == K and offsets.numel() == E + 1, "shape mismatch")
+    code = _out_code(out_dtype)
+    C = _out_tensor(C, (T, N), code, A.device)
+    with torch.cuda.device(A.device):
+        _check("fp8_grouped_gemm", lib.fp8_grouped_gemm(_ptr(A), _ptr(B), _ptr(offsets), E, _ptr(scale_a),
+                                                        _ptr(scale_b), _ptr(C), T, N, K,
+                                                        code | (FP8_ACC_FAST if fast else 0),
+                                                        _stream(A.device, stream)))
+    return C

@@ -1,0 +1,151 @@
+// C ABI (include/fp8gemm.h): argument validation on the host, then the
+// launchers.  Nothing here allocates, synchronises or touches the GPU before
+// every check has passed, so the error paths run without a device.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdint.h>
+
+#include "../../include/fp8gemm.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fp8_status fail(fp8_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+fp8_status ok() {
+    g_err[0] = '\0';
+    return FP8_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+fp8_status from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(FP8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxK = int64_t(1) << 23;  // 256 rows x K stays below 2^31 bytes per tile
+constexpr int64_t kMaxN = int64_t(1) << 20;  // 256 K-rows x N stays below 2^31 bytes per step
+
+fp8_status check_gemm_common(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
+                             int32_t out_dtype) {
+    if (M < 0 || N < 0 || K < 0) return fail(FP8_ERR_INVALID_ARG, "negative size (M=%lld N=%lld K=%lld)",
+                                             (long long)M, (long long)N, (long long)K);
+    // an operand with no elements may be null
+    if ((!A && M * K > 0) || (!B && K * N > 0) || (!C && M * N > 0))
+        return fail(FP8_ERR_INVALID_ARG, "null matrix pointer");
+    const int32_t base = out_dtype & ~FP8_ACC_FAST;
+    if (base != FP8_OUT_F32 && base != FP8_OUT_BF16)
+        return fail(FP8_ERR_INVALID_ARG, "out_dtype %#x is neither FP8_OUT_F32 nor FP8_OUT_BF16 (| FP8_ACC_FAST)",
+                    out_dtype);
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return fail(FP8_ERR_INVALID_ARG, "A, B and C must be 16-byte aligned");
+    if (K > kMaxK) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld exceeds 2^23", (long long)K);
+    if (N > kMaxN) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "N=%lld exceeds 2^20", (long long)N);
+    if (M > (int64_t(1) << 31) - 1) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "M=%lld exceeds 2^31-1", (long long)M);
+    return FP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_string(int32_t status) {
+    switch (status) {
+        case FP8_OK: return "FP8_OK";
+        case FP8_ERR_INVALID_ARG: return "FP8_ERR_INVALID_ARG";
+        case FP8_ERR_UNSUPPORTED_SHAPE: return "FP8_ERR_UNSUPPORTED_SHAPE";
+        case FP8_ERR_HIP: return "FP8_ERR_HIP";
+        default: return "FP8_ERR_UNKNOWN";
+    }
+}
+
+const char* fp8_last_error(void) { return g_err; }
+
+fp8_status fp8_quantize(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, void* stream) {
+    if (n < 0) return fail(FP8_ERR_INVALID_ARG, "negative n=%lld", (long long)n);
+    if (!scale || !amax || (n > 0 && (!x || !q))) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
+    if (scale == amax) return fail(FP8_ERR_INVALID_ARG, "scale and amax must be distinct");
+    return from_hip(fp8k::launch_quantize_pertensor(x, n, q, scale, amax, (hipStream_t)stream), "fp8_quantize");
+}
+
+fp8_status fp8_quantize_blocked(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* tile_scales,
+                                void* stream) {
+    if (!x || !q || !tile_scales) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
+    if (rows < 0 || cols < 0) return fail(FP8_ERR_INVALID_ARG, "negative size");
+    if (rows % 32 || cols % 32)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "rows=%lld and cols=%lld must be multiples of 32", (long long)rows,
+                    (long long)cols);
+    if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
+    if ((rows / 32) * (cols / 32) > (int64_t(1) << 34))
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "too many tiles");
+    return from_hip(fp8k::launch_quantize_blocked(x, rows, cols, q, tile_scales, (hipStream_t)stream),
+                    "fp8_quantize_blocked");
+}
+
+fp8_status fp8_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
+                                uint8_t* q, float* scales, float* amax, void* stream) {
+    if (!x || !q || !scales || !amax || !offsets) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
+    if (rows < 0 || cols < 0) return fail(FP8_ERR_INVALID_ARG, "negative size");
+    if (groups < 1 || groups > 1024) return fail(FP8_ERR_INVALID_ARG, "groups=%d outside [1, 1024]", groups);
+    if (cols % 4) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "cols=%lld must be a multiple of 4", (long long)cols);
+    if (rows > (int64_t(1) << 31) - 1) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "rows exceed 2^31-1");
+    if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
+    if (scales == amax) return fail(FP8_ERR_INVALID_ARG, "scales and amax must be distinct");
+    return from_hip(fp8k::launch_quantize_grouped(x, rows, cols, offsets, groups, q, scales, amax, (hipStream_t)stream),
+                    "fp8_quantize_grouped");
+}
+
+fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
+                    int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
+    fp8_status st = check_gemm_common(A, B, C, M, N, K, out_dtype);
+    if (st != FP8_OK) return st;
+    if (!scale_a || !scale_b) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
+    if (K % 16 || N % 16)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld and N=%lld must be multiples of 16", (long long)K, (long long)N);
+    if (M == 0 || N == 0) return ok();
+    fp8k::GemmProblem g{A, B, C, scale_a, scale_b, nullptr, 0, M, N, K,
+                        (out_dtype & ~FP8_ACC_FAST) == FP8_OUT_BF16, (out_dtype & FP8_ACC_FAST) != 0};
+    return from_hip(fp8k::launch_gemm(g, (hipStream_t)stream), "fp8_gemm");
+}
+
+fp8_status fp8_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,
+                                int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
+    fp8_status st = check_gemm_common(A, B, C, M, N, K, out_dtype);
+    if (st != FP8_OK) return st;
+    if (!s_a || !s_b) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
+    if (out_dtype & FP8_ACC_FAST)
+        return fail(FP8_ERR_INVALID_ARG, "FP8_ACC_FAST is not available for the block-scaled GEMM");
+    if (M % 32 || N % 32 || K % 32)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "M=%lld N=%lld K=%lld must be multiples of 32", (long long)M,
+                    (long long)N, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    return from_hip(fp8k::launch_gemm_blockscaled(A, B, s_a, s_b, C, M, N, K, out_dtype == FP8_OUT_BF16,
+                                                  (hipStream_t)stream),
+                    "fp8_gemm_blockscaled");
+}
+
+fp8_status fp8_grouped_gemm(const uint8_t* A, const uint8_t* B, const int32_t* offsets, int32_t experts,
+                            const float* scale_a, const float* scale_b, void* C, int64_t T, int64_t N, int64_t K,
+                            int32_t out_dtype, void* stream) {
+    fp8_status st = check_gemm_common(A, B, C, T, N, K, out_dtype);
+    if (st != FP8_OK) return st;
+    if (!scale_a || !scale_b || !offsets) return fail(FP8_ERR_INVALID_ARG, "null scale or offsets pointer");
+    if (experts < 1 || experts > 1024) return fail(FP8_ERR_INVALID_ARG, "experts=%d outside [1, 1024]", experts);
+    if (K % 16 || N % 16)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld and N=%lld must be multiples of 16", (long long)K, (long long)N);
+    if (T == 0 || N == 0) return ok();
+    fp8k::GemmProblem g{A, B, C, scale_a, scale_b, offsets, experts, T, N, K,
+                        (out_dtype & ~FP8_ACC_FAST) == FP8_OUT_BF16, (out_dtype & FP8_ACC_FAST) != 0};
+    return from_hip(fp8k::launch_gemm(g, (hipStream_t)stream), "fp8_grouped_gemm");
+}
+
+}  // extern "C"

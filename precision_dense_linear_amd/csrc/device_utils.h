@@ -1,0 +1,115 @@
+// Device-side building blocks shared by the FP8 kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8k {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Buffer resource over [base, base + bytes).  Raw (stride 0) buffer loads whose
+// offset is at or beyond `bytes` return zero and touch no memory; the kernels
+// use this to zero-fill ragged tiles without any out-of-bounds access.
+// dword3 0x00020000 is the gfx9 raw 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Offset that is out of range for every resource built with at most 2^31 bytes.
+constexpr uint32_t OOB = 0x80000000u;
+
+__device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
+    return bytes <= 0 ? 0u : (bytes >= (int64_t)OOB ? OOB : (uint32_t)bytes);
+}
+
+// One wave stores 64 x 16 bytes from global memory straight into LDS: lane l's
+// 16 bytes land at lds_wave_base + 16*l (buffer_load_dwordx4 ... lds).
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, lds_u8* lds_wave_base, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
+// D = A(32x64) * B(64x32) + C with OCP E4M3 operands, FP32 accumulate
+// (v_mfma_f32_32x32x64_f8f6f4; zero scale operands select the unscaled form).
+// Lane l holds A row l%32 / B column l%32, K bytes 32*(l/32) .. +31;
+// accumulator element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+__device__ __forceinline__ v16f mfma_32x32x64_e4m3(v8i a, v8i b, v16f c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// D = A(32x16) * B(16x32) + C in BF16 with FP32 accumulate
+// (v_mfma_f32_32x32x16_bf16).  Lane l holds A row l%32 / B column l%32, K
+// elements 8*(l/32) .. +7; accumulator layout as for the 32x32x64 form.
+// Unlike the FP8 forms (which align each group of 8 products to a 13-bit
+// window below the group's largest product and truncate the rest), every
+// product of two E4M3 values reaches the FP32 accumulator exactly here.
+__device__ __forceinline__ v16f mfma_32x32x16_bf16(v8bf a, v8bf b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight E4M3 codes (two dwords, code 0 in the low byte) -> eight BF16 values.
+// Every E4M3 value is a BF16 value, and the scale is 1, so this is exact
+// (v_cvt_scalef32_pk_bf16_fp8, two codes per instruction).
+__device__ __forceinline__ v8bf e4m3x8_to_bf16(int lo, int hi) {
+    const v2bf r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)lo, 1.0f, false);
+    const v2bf r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)lo, 1.0f, true);
+    const v2bf r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)hi, 1.0f, false);
+    const v2bf r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)hi, 1.0f, true);
+    return (v8bf){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// 8-byte LDS transpose read (ds_read_b64_tr_b8).  Within each 16-lane group,
+// output lane 8h + c receives byte c of the 8-byte rows addressed by lanes
+// 2j + h, j = 0..7 (row j in byte j of the result).
+__device__ __forceinline__ v2i lds_read_tr8(const lds_u8* p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
+}
+
+__device__ __forceinline__ v4i lds_read16(const lds_u8* p) {
+    return *(const __attribute__((address_space(3))) v4i*)p;
+}
+
+// binary32 -> bfloat16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Four binary32 values -> four E4M3 codes (RNE), saturating at +-448: the
+// clamp comes first because the converter alone maps |v| > 464 to NaN.
+__device__ __forceinline__ uint32_t e4m3x4_sat(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint8_t e4m3_sat(float a) {
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(a, 0.0f, 0, false) & 0xFF);
+}
+
+// scale = amax / 448 (IEEE binary32 division); 1 for an all-zero group.
+__device__ __forceinline__ float scale_from_amax(float amax) {
+    return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+}
+
+}  // namespace fp8k

@@ -1,0 +1,36 @@
+// Host-side launchers behind the C ABI (fp8gemm.h).  Arguments have already
+// been validated by the entry points; each launcher only enqueues kernels on
+// `s` and returns the first HIP error it sees.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8k {
+
+hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, hipStream_t s);
+hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* tile_scales,
+                                   hipStream_t s);
+hipError_t launch_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
+                                   uint8_t* q, float* scales, float* amax, hipStream_t s);
+
+// Dense GEMM on E4M3 codes; `experts` > 0 selects the grouped (MoE) problem,
+// where M is the total row count T and B holds `experts` K x N matrices.
+struct GemmProblem {
+    const uint8_t* A;
+    const uint8_t* B;
+    void* C;
+    const float* scale_a;
+    const float* scale_b;
+    const int32_t* offsets;  // grouped only
+    int32_t experts;         // 0 for the plain GEMM
+    int64_t M, N, K;
+    int32_t out_bf16;
+    int32_t fast_acc;  // 1: native FP8 MFMA accumulation; 0: exact products (BF16 MFMA)
+};
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
+
+hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,
+                                   int64_t M, int64_t N, int64_t K, int32_t out_bf16, hipStream_t s);
+
+}  // namespace fp8k

@@ -1,0 +1,230 @@
+// Input side of the scaled FP8 GEMM: amax reduction and E4M3 quantization.
+//
+// Per-tensor scaling keeps values inside the E4M3 range +-448 ("Triton FP8
+// GEMM via CUTLASS naming", risk paragraph and the scale_max 448 item of its
+// parameter list); 32x32 block scales follow the parameter paragraph of "FP8
+// GEMM in JAX with Triton for Blackwell".  In every mode:
+//     scale = amax / 448 (IEEE binary32 division, 1 for amax == 0)
+//     code  = E4M3_RNE(clamp(fl32(x / scale), -448, 448))
+// All kernels are HBM-bound streams: 16-byte loads, 16-byte code stores.
+#include "device_utils.h"
+#include "launch.h"
+
+namespace fp8k {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void fill_f32(float* p, int n, float v) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// Block-level max of non-negative values, then one atomicMax on the float's
+// bit pattern (order-preserving for non-negative floats).
+__device__ __forceinline__ void block_max_to(float m, float* dst) {
+    __shared__ float red[kThreads / 64];
+    m = wave_max(m);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float r = red[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+        atomicMax(reinterpret_cast<unsigned int*>(dst), __float_as_uint(r));
+    }
+}
+
+// amax over n floats (x 16-byte aligned); grid-stride over v4fs.
+__global__ void __launch_bounds__(kThreads) amax_kernel(const float* __restrict__ x, int64_t n, float* amax) {
+    const int64_t n4 = n >> 2;
+    const v4f* x4 = reinterpret_cast<const v4f*>(x);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    float m = 0.0f;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        v4f v = __builtin_nontemporal_load(&x4[i]);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        m = fmaxf(m, fabsf(x[i]));
+    block_max_to(m, amax);
+}
+
+// codes for n floats with the scale derived from *amax; thread t handles 16
+// consecutive elements per iteration (four v4f loads, one 16-byte store).
+__global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restrict__ x, int64_t n,
+                                                            const float* __restrict__ amax, uint8_t* __restrict__ q,
+                                                            float* scale_out) {
+    const float s = scale_from_amax(*amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+    const int64_t n16 = n >> 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const v4f* x4 = reinterpret_cast<const v4f*>(x);
+    uint4* q16 = reinterpret_cast<uint4*>(q);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        v4f v0 = __builtin_nontemporal_load(&x4[4 * i + 0]);
+        v4f v1 = __builtin_nontemporal_load(&x4[4 * i + 1]);
+        v4f v2 = __builtin_nontemporal_load(&x4[4 * i + 2]);
+        v4f v3 = __builtin_nontemporal_load(&x4[4 * i + 3]);
+        uint4 o;
+        o.x = e4m3x4_sat(__fdiv_rn(v0.x, s), __fdiv_rn(v0.y, s), __fdiv_rn(v0.z, s), __fdiv_rn(v0.w, s));
+        o.y = e4m3x4_sat(__fdiv_rn(v1.x, s), __fdiv_rn(v1.y, s), __fdiv_rn(v1.z, s), __fdiv_rn(v1.w, s));
+        o.z = e4m3x4_sat(__fdiv_rn(v2.x, s), __fdiv_rn(v2.y, s), __fdiv_rn(v2.z, s), __fdiv_rn(v2.w, s));
+        o.w = e4m3x4_sat(__fdiv_rn(v3.x, s), __fdiv_rn(v3.y, s), __fdiv_rn(v3.z, s), __fdiv_rn(v3.w, s));
+        q16[i] = o;
+    }
+    for (int64_t i = (n16 << 4) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        q[i] = e4m3_sat(__fdiv_rn(x[i], s));
+}
+
+// 32x32 tiles: one wave per tile.  Lane l covers row l/2 of the tile, columns
+// 16*(l%2) .. +15: amax over the tile by a wave reduction, then the codes.
+__global__ void __launch_bounds__(kThreads) quantize_blocked_kernel(const float* __restrict__ x, int64_t rows,
+                                                                    int64_t cols, uint8_t* __restrict__ q,
+                                                                    float* __restrict__ tile_scales) {
+    const int64_t tiles_c = cols >> 5;
+    const int64_t ntiles = (rows >> 5) * tiles_c;
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (tile >= ntiles) return;
+    const int64_t ti = tile / tiles_c, tj = tile % tiles_c;
+    const int64_t r = ti * 32 + (lane >> 1);
+    const int64_t c = tj * 32 + (lane & 1) * 16;
+    const v4f* src = reinterpret_cast<const v4f*>(x + r * cols + c);
+    v4f v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(&src[j]);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+    m = wave_max(m);
+    const float s = scale_from_amax(m);
+    if (lane == 0) tile_scales[tile] = s;
+    uint4 o;
+    o.x = e4m3x4_sat(__fdiv_rn(v[0].x, s), __fdiv_rn(v[0].y, s), __fdiv_rn(v[0].z, s), __fdiv_rn(v[0].w, s));
+    o.y = e4m3x4_sat(__fdiv_rn(v[1].x, s), __fdiv_rn(v[1].y, s), __fdiv_rn(v[1].z, s), __fdiv_rn(v[1].w, s));
+    o.z = e4m3x4_sat(__fdiv_rn(v[2].x, s), __fdiv_rn(v[2].y, s), __fdiv_rn(v[2].z, s), __fdiv_rn(v[2].w, s));
+    o.w = e4m3x4_sat(__fdiv_rn(v[3].x, s), __fdiv_rn(v[3].y, s), __fdiv_rn(v[3].z, s), __fdiv_rn(v[3].w, s));
+    *reinterpret_cast<uint4*>(q + r * cols + c) = o;
+}
+
+// Group of row r by binary search over the (already clamped) boundaries held
+// in LDS; returns -1 for rows outside every group.
+__device__ __forceinline__ int find_group(const int64_t* bnd, int groups, int64_t r) {
+    if (r < bnd[0] || r >= bnd[groups]) return -1;
+    int lo = 0, hi = groups;  // bnd[lo] <= r < bnd[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (bnd[mid] <= r) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void load_bounds(const int32_t* off, int groups, int64_t rows, int64_t* bnd) {
+    // Clamp sequentially in thread 0 (groups <= 1024: negligible).
+    if (threadIdx.x == 0) {
+        int64_t lo = 0;
+        for (int g = 0; g <= groups; ++g) {
+            int64_t v = off[g];
+            v = v < lo ? lo : (v > rows ? rows : v);
+            bnd[g] = v;
+            lo = v;
+        }
+    }
+    __syncthreads();
+}
+
+// Grouped amax: each wave reduces whole rows (cols % 4 == 0) and folds the row
+// max into its group's amax with one atomicMax per row.
+__global__ void __launch_bounds__(kThreads) amax_grouped_kernel(const float* __restrict__ x, int64_t rows, int64_t cols,
+                                                                const int32_t* __restrict__ off, int groups,
+                                                                float* amax) {
+    __shared__ int64_t bnd[1025];
+    load_bounds(off, groups, rows, bnd);
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+    const int64_t c4 = cols >> 2;
+    for (int64_t r = wave; r < rows; r += nwaves) {
+        const int g = find_group(bnd, groups, r);
+        if (g < 0) continue;
+        const v4f* src = reinterpret_cast<const v4f*>(x + r * cols);
+        float m = 0.0f;
+        for (int64_t j = lane; j < c4; j += 64) {
+            v4f v = __builtin_nontemporal_load(&src[j]);
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+        m = wave_max(m);
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(amax + g), __float_as_uint(m));
+    }
+}
+
+// Grouped quantize: rows are processed one per wave (lane j takes v4f j,
+// j+64, ...); each row uses its group's scale.  Block 0 also writes scales.
+__global__ void __launch_bounds__(kThreads) quantize_grouped_kernel(const float* __restrict__ x, int64_t rows,
+                                                                    int64_t cols, const int32_t* __restrict__ off,
+                                                                    int groups, const float* __restrict__ amax,
+                                                                    uint8_t* __restrict__ q, float* scales) {
+    __shared__ int64_t bnd[1025];
+    load_bounds(off, groups, rows, bnd);
+    if (blockIdx.x == 0)
+        for (int g = threadIdx.x; g < groups; g += blockDim.x) scales[g] = scale_from_amax(amax[g]);
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+    const int64_t c4 = cols >> 2;
+    for (int64_t r = wave; r < rows; r += nwaves) {
+        const int g = find_group(bnd, groups, r);
+        if (g < 0) continue;
+        const float s = scale_from_amax(amax[g]);
+        const v4f* src = reinterpret_cast<const v4f*>(x + r * cols);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(q + r * cols);
+        for (int64_t j = lane; j < c4; j += 64) {
+            v4f v = __builtin_nontemporal_load(&src[j]);
+            dst[j] = e4m3x4_sat(__fdiv_rn(v.x, s), __fdiv_rn(v.y, s), __fdiv_rn(v.z, s), __fdiv_rn(v.w, s));
+        }
+    }
+}
+
+int stream_blocks(int64_t work_items, int per_block) {
+    int64_t b = (work_items + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > 256 * 16) b = 256 * 16;  // 16 blocks per CU on 256 CUs; grid-stride beyond
+    return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, hipStream_t s) {
+    hipLaunchKernelGGL(fill_f32, dim3(1), dim3(64), 0, s, amax, 1, 0.0f);
+    if (n > 0) hipLaunchKernelGGL(amax_kernel, dim3(stream_blocks(n / 4 + 1, kThreads)), dim3(kThreads), 0, s, x, n, amax);
+    hipLaunchKernelGGL(quantize_kernel, dim3(stream_blocks(n / 16 + 1, kThreads)), dim3(kThreads), 0, s, x, n,
+                       (const float*)amax, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* tile_scales,
+                                   hipStream_t s) {
+    const int64_t ntiles = (rows / 32) * (cols / 32);
+    if (ntiles == 0) return hipSuccess;
+    const int64_t blocks = (ntiles + kThreads / 64 - 1) / (kThreads / 64);
+    hipLaunchKernelGGL(quantize_blocked_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, rows, cols, q,
+                       tile_scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
+                                   uint8_t* q, float* scales, float* amax, hipStream_t s) {
+    hipLaunchKernelGGL(fill_f32, dim3((groups + 255) / 256), dim3(256), 0, s, amax, groups, 0.0f);
+    const int blocks = stream_blocks(rows, kThreads / 64);
+    if (rows > 0 && cols > 0)
+        hipLaunchKernelGGL(amax_grouped_kernel, dim3(blocks), dim3(kThreads), 0, s, x, rows, cols, offsets, groups,
+                           amax);
+    hipLaunchKernelGGL(quantize_grouped_kernel, dim3(blocks), dim3(kThreads), 0, s, x, rows, cols, offsets, groups,
+                       (const float*)amax, q, scales);
+    return hipGetLastError();
+}
+
+}  // namespace fp8k

@@ -1,0 +1,70 @@
+"""Comparison of HIP outputs with the CPU oracle, to the stated bounds.
+
+* Codes, scales and amax: bit-exact.
+* FP32 output: |C_gpu - C_exact| <= 2e-6 * sum_k |a_ik * b_kj| * scale_a * scale_b.
+* BF16 output: the GPU value is within 1 BF16 ulp (in the monotone ordering of
+  BF16 bit patterns) of the oracle's correctly rounded value.  Where the FP32
+  bound above exceeds half a BF16 ulp of the exact value (heavy cancellation,
+  where an FP32 accumulator cannot resolve the BF16 rounding), an element
+  also passes if |C_gpu - C_exact| <= FP32 bound + 1 BF16 ulp; such elements
+  are counted and reported separately.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+REL_F32 = 2e-6
+
+
+def bf16_ord(bits: np.ndarray) -> np.ndarray:
+    b = bits.astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    ax = np.abs(x)
+    _, e = np.frexp(ax)                 # ax = f * 2^e, 0.5 <= f < 1
+    ulp = np.ldexp(1.0, e - 8)          # 8 significand bits
+    return np.maximum(ulp, 2.0 ** -133)
+
+
+def check_f32(c_gpu: np.ndarray, exact: np.ndarray, sumabs_scaled: np.ndarray, what: str = ""):
+    c = c_gpu.astype(np.float64)
+    bound = REL_F32 * sumabs_scaled + 1e-15 * np.abs(exact)
+    err = np.abs(c - exact)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.argmax(np.where(bad, err / np.maximum(bound, 1e-300), 0))
+        raise AssertionError("%s: %d of %d FP32 outputs outside 2e-6*sum|ab| (worst: got %r exact %r bound %r)"
+                             % (what, int(bad.sum()), c.size, c.flat[i], exact.flat[i], bound.flat[i]))
+    return float(np.max(err / np.maximum(bound, 1e-300))) if c.size else 0.0
+
+
+def check_bf16(c_bits: np.ndarray, oracle_bits: np.ndarray, exact: np.ndarray, sumabs_scaled: np.ndarray,
+               what: str = ""):
+    """Returns (max ulp distance, count passed only under the cancellation allowance)."""
+    d = np.abs(bf16_ord(c_bits) - bf16_ord(oracle_bits))
+    ok = d <= 1
+    fbound = REL_F32 * sumabs_scaled
+    cancel = fbound > 0.5 * bf16_ulp(exact)
+    alt = cancel & (np.abs(bf16_to_f64(c_bits) - exact) <= fbound + bf16_ulp(exact))
+    extra = (~ok) & alt
+    bad = (~ok) & (~alt)
+    if bad.any():
+        i = int(np.argmax(np.where(bad, d, -1)))
+        raise AssertionError("%s: %d of %d BF16 outputs more than 1 ulp from the oracle (worst %d ulp: got %#06x "
+                             "want %#06x, exact %r)" % (what, int(bad.sum()), d.size, int(d.flat[i]),
+                                                        int(c_bits.flat[i]), int(oracle_bits.flat[i]), exact.flat[i]))
+    return int(d[ok].max()) if ok.any() else 0, int(extra.sum())
+
+
+def to_bits(c) -> np.ndarray:
+    """A torch output tensor (float32 or bfloat16) -> numpy bits (uint32 / uint16)."""
+    import torch
+    if c.dtype == torch.bfloat16:
+        return c.view(torch.int16).cpu().numpy().view(np.uint16)
+    return c.cpu().numpy().view(np.uint32)

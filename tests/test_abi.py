@@ -1,0 +1,109 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and rejects bad arguments on the host before launching
+anything (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_dense_linear_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8gemm.h")
+
+# Any non-null address works for the validation paths: none of these calls
+# reaches a launch, so the pointers are never dereferenced.
+FAKE = ctypes.c_void_p(0x100000)
+FAKE_ODD = ctypes.c_void_p(0x100008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fp8_quantize", "fp8_quantize_blocked", "fp8_quantize_grouped", "fp8_gemm",
+              "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_status_string", "fp8_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(P.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(P.SYMBOLS)
+
+
+def test_status_strings():
+    assert P.status_name(0) == "FP8_OK"
+    assert P.status_name(1) == "FP8_ERR_INVALID_ARG"
+    assert P.status_name(2) == "FP8_ERR_UNSUPPORTED_SHAPE"
+    assert P.status_name(3) == "FP8_ERR_HIP"
+    assert P.status_name(99) == "FP8_ERR_UNKNOWN"
+
+
+def gemm(A=FAKE, B=FAKE, sa=FAKE, sb=FAKE, C=FAKE, M=64, N=64, K=64, out=1):
+    return P.lib.fp8_gemm(A, B, sa, sb, C, M, N, K, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=None), P.FP8_ERR_INVALID_ARG),
+    (dict(A=None, M=0), P.FP8_OK),        # an empty operand may be null (M == 0: nothing is launched)
+    (dict(B=None), P.FP8_ERR_INVALID_ARG),
+    (dict(C=None), P.FP8_ERR_INVALID_ARG),
+    (dict(sa=None), P.FP8_ERR_INVALID_ARG),
+    (dict(M=-1), P.FP8_ERR_INVALID_ARG),
+    (dict(K=-16), P.FP8_ERR_INVALID_ARG),
+    (dict(out=7), P.FP8_ERR_INVALID_ARG),
+    (dict(A=FAKE_ODD), P.FP8_ERR_INVALID_ARG),
+    (dict(K=40), P.FP8_ERR_UNSUPPORTED_SHAPE),
+    (dict(N=40), P.FP8_ERR_UNSUPPORTED_SHAPE),
+    (dict(K=(1 << 23) + 16), P.FP8_ERR_UNSUPPORTED_SHAPE),
+    (dict(M=0), P.FP8_OK),            # empty: nothing to enqueue
+    (dict(N=0), P.FP8_OK),
+])
+def test_gemm_validation(kw, status):
+    assert gemm(**kw) == status
+    if status != P.FP8_OK:
+        assert P.lib.fp8_last_error().decode() != ""
+
+
+def test_blockscaled_validation():
+    f = P.lib.fp8_gemm_blockscaled
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 48, 64, 64, 1, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 48, 1, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 1, None) == P.FP8_OK
+
+
+def test_grouped_validation():
+    f = P.lib.fp8_grouped_gemm
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, 1025, FAKE, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, 8, FAKE, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, 64, 64, 40, 1, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert f(FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, 0, 64, 64, 1, None) == P.FP8_OK
+
+
+def test_quantize_validation():
+    L = P.lib
+    assert L.fp8_quantize(None, 16, FAKE, FAKE, FAKE, None) == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize(FAKE, -1, FAKE, FAKE, FAKE, None) == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize(FAKE_ODD, 16, FAKE, FAKE, ctypes.c_void_p(0x200000), None) == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize(FAKE, 16, FAKE, FAKE, FAKE, None) == P.FP8_ERR_INVALID_ARG   # scale aliases amax
+    assert L.fp8_quantize_blocked(FAKE, 48, 64, FAKE, FAKE, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert L.fp8_quantize_blocked(FAKE, 64, 64, None, FAKE, None) == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize_grouped(FAKE, 64, 64, FAKE, 0, FAKE, FAKE, ctypes.c_void_p(0x200000), None) \
+        == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize_grouped(FAKE, 64, 6, FAKE, 2, FAKE, FAKE, ctypes.c_void_p(0x200000), None) \
+        == P.FP8_ERR_UNSUPPORTED_SHAPE
+
+
+def test_binding_refuses_wrong_operand_dtype():
+    import torch
+    with pytest.raises(TypeError):
+        P._codes(torch.zeros(4, dtype=torch.float16))

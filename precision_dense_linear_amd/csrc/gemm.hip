@@ -24,9 +24,17 @@ namespace fp8k {
 
 namespace {
 
+// Operand fragments of one 64-byte K slice for a wave: TM A blocks, TN B blocks.
+template <int TM, int TN>
+struct Frags {
+    v8i a[TM];
+    v8i b[TN];
+};
+
 template <int BM, int BN, int WM, int WN, int KS, int GROUP_M, bool BF16, bool EXACT>
 __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     using C = TileCfg<BM, BN, WM, WN, KS>;
+    constexpr int TM = C::TM, TN = C::TN;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
     const TileSlice t = resolve_tile<BM, BN, GROUP_M>(p);
@@ -40,75 +48,136 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     const int64_t K = p.K, N = p.N;
     const int nsteps = (int)((K + KS * BK - 1) / (KS * BK));
     lds_u8* lds = (lds_u8*)smem;
+    const StageLoader<BM, BN, WM, WN, KS> loader(t, N, K, wave, lane);
 
-    v16f acc[C::TM][C::TN];
+    v16f acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int a_row0 = wm * C::WTM + (lane & 31);
-    const int a_c0 = (lane >> 5) * 2;
-    const int b_krow0 = (lane >> 5) * 32 + ((lane & 15) >> 1);
-    const int b_col0 = wn * C::WTN + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-
-    if (nsteps > 0) load_stage<BM, BN, WM, WN, KS>(t, N, K, 0, lds, wave, lane);
-    for (int step = 0; step < nsteps; ++step) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's stage loads have landed in LDS
-        __syncthreads();                // ... and every wave's; the other buffer is free
-        if (step + 1 < nsteps)
-            load_stage<BM, BN, WM, WN, KS>(t, N, K, (int64_t)(step + 1) * (KS * BK), lds + ((step + 1) & 1) * C::STAGE,
-                                           wave, lane);
-
-        const lds_u8* As = lds + (step & 1) * C::STAGE + ks * BM * BK;
-        const lds_u8* Bs = lds + (step & 1) * C::STAGE + C::A_STAGE + ks * BK * BN;
+    // Per-lane LDS byte offsets of this wave's operands inside a stage.
+    int a_off[TM][2];  // [block][64-byte slice]: chunk pair start of row (lane%32)
+    int b_off[TN][2][4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            v8i a[C::TM], b[C::TN];
+    for (int mi = 0; mi < TM; ++mi) {
+        const int row = wm * C::WTM + mi * 32 + (lane & 31);
 #pragma unroll
-            for (int mi = 0; mi < C::TM; ++mi) {
-                const int row = a_row0 + mi * 32;
-                const int c = s * 4 + a_c0;
-                const v4i lo = lds_read16(As + row * BK + swz_a(row, c) * 16);
-                const v4i hi = lds_read16(As + row * BK + swz_a(row, c + 1) * 16);
-                a[mi] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int s = 0; s < 2; ++s) a_off[mi][s] = ks * BM * BK + row * BK + swz_a(row, s * 4 + (lane >> 5) * 2) * 16;
+    }
+    // the second chunk of the pair sits at position (c+1) ^ swz = (c ^ swz) ^ 1: i.e. +/-16 bytes
+    const int a_pair = (((lane & 31) >> 1) & 1) ? -16 : 16;
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni) {
+        const int col = wn * C::WTN + ni * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int tq = 0; tq < 4; ++tq) {
+                const int kr = s * 64 + (lane >> 5) * 32 + ((lane & 15) >> 1) + 8 * tq;
+                b_off[ni][s][tq] = C::A_STAGE + ks * BK * BN + kr * BN + swz_b<BN>(kr, col >> 4) * 16 + (col & 15);
             }
+    }
+
+    auto read_frags = [&](const lds_u8* stage, int s, Frags<TM, TN>& f) {
 #pragma unroll
-            for (int ni = 0; ni < C::TN; ++ni) {
-                const int col = b_col0 + ni * 32;
-                v2i part[4];
+        for (int mi = 0; mi < TM; ++mi) {
+            const v4i lo = lds_read16(stage + a_off[mi][s]);
+            const v4i hi = lds_read16(stage + a_off[mi][s] + a_pair);
+            f.a[mi] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
 #pragma unroll
-                for (int tq = 0; tq < 4; ++tq) {
-                    const int kr = s * 64 + b_krow0 + 8 * tq;
-                    part[tq] = lds_read_tr8(Bs + kr * BN + swz_b<BN>(kr, col >> 4) * 16 + (col & 15));
-                }
-                b[ni] = (v8i){part[0][0], part[0][1], part[1][0], part[1][1],
-                              part[2][0], part[2][1], part[3][0], part[3][1]};
-            }
+        for (int ni = 0; ni < TN; ++ni) {
+            v2i q[4];
+#pragma unroll
+            for (int tq = 0; tq < 4; ++tq) q[tq] = lds_read_tr8(stage + b_off[ni][s][tq]);
+            f.b[ni] = (v8i){q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+        }
+    };
+
+    // The MFMAs of one 64-byte slice, blocks [first, last) in (mi, ni) order.
+    auto mma = [&](const Frags<TM, TN>& f, int first, int last) {
+#pragma unroll
+        for (int idx = 0; idx < TM * TN; ++idx) {
+            if (idx < first || idx >= last) continue;
+            const int mi = idx / TN, ni = idx % TN;
             if constexpr (EXACT) {
-                // four K=16 BF16 MFMAs per 64-byte slice; chunk c of each lane's
-                // 32 bytes (K 32*(l/32) + 8c .. +7) feeds the c-th one, for A and B alike
+                // four K=16 BF16 MFMAs; chunk c of each lane's 32 bytes
+                // (K 32*(l/32) + 8c .. +7) feeds the c-th, for A and B alike
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    v8bf ab[C::TM], bb[C::TN];
-#pragma unroll
-                    for (int mi = 0; mi < C::TM; ++mi) ab[mi] = e4m3x8_to_bf16(a[mi][2 * c], a[mi][2 * c + 1]);
-#pragma unroll
-                    for (int ni = 0; ni < C::TN; ++ni) bb[ni] = e4m3x8_to_bf16(b[ni][2 * c], b[ni][2 * c + 1]);
-#pragma unroll
-                    for (int mi = 0; mi < C::TM; ++mi)
-#pragma unroll
-                        for (int ni = 0; ni < C::TN; ++ni) acc[mi][ni] = mfma_32x32x16_bf16(ab[mi], bb[ni], acc[mi][ni]);
-                }
+                for (int c = 0; c < 4; ++c)
+                    acc[mi][ni] = mfma_32x32x16_bf16(e4m3x8_to_bf16(f.a[mi][2 * c], f.a[mi][2 * c + 1]),
+                                                     e4m3x8_to_bf16(f.b[ni][2 * c], f.b[ni][2 * c + 1]), acc[mi][ni]);
             } else {
-#pragma unroll
-                for (int mi = 0; mi < C::TM; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < C::TN; ++ni) acc[mi][ni] = mfma_32x32x64_e4m3(a[mi], b[ni], acc[mi][ni]);
+                acc[mi][ni] = mfma_32x32x64_e4m3(f.a[mi], f.b[ni], acc[mi][ni]);
             }
         }
+    };
+
+    // Pipeline, per 128-byte step k (LDS buffer k&1; fragments f0/f1 for its
+    // two 64-byte slices; f0 was read at the end of step k-1):
+    //   read the slice-1 fragments f1 -- before any new global->LDS load is
+    //   in flight, so these LDS reads need no wait on them;
+    //   issue the global loads of stage k+1 into the other buffer;
+    //   slice-0 MFMAs (f0), then all but the last TAIL slice-1 MFMAs;
+    //   wait for stage k+1 and barrier: it is in LDS, and buffer k&1 is free;
+    //   read stage k+1's slice-0 fragments f0 under the last TAIL MFMAs.
+    // The body is branch-free (past the end of K the loads are empty), and
+    // sched_barrier keeps the compiler from moving MFMAs across the barrier.
+    constexpr int TAIL = (TM * TN) >= 8 ? 4 : ((TM * TN) >= 2 ? (TM * TN) / 2 : 1);
+    Frags<TM, TN> f0, f1;
+    if (nsteps > 0) {
+        loader.issue(0, lds);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        read_frags(lds, 0, f0);
+    }
+    // MFMA instructions per 64-byte slice, LDS reads per fragment set, and
+    // global->LDS loads per stage, for the interleave below.
+    constexpr int MF = TM * TN * (EXACT ? 4 : 1);
+    constexpr int MF_TAIL = TAIL * (EXACT ? 4 : 1);
+    constexpr int RD = 2 * TM + 4 * TN;
+    constexpr int LD = StageLoader<BM, BN, WM, WN, KS>::NA + StageLoader<BM, BN, WM, WN, KS>::NB;
+    for (int step = 0; step < nsteps; ++step) {
+        const lds_u8* cur = lds + (step & 1) * C::STAGE;
+        lds_u8* nxt = lds + ((step + 1) & 1) * C::STAGE;
+        read_frags(cur, 1, f1);
+        loader.issue((int64_t)(step + 1) * (KS * BK), nxt);
+        mma(f0, 0, TM * TN);
+        mma(f1, 0, TM * TN - TAIL);
+        // order: the f1 reads spread over the first slice-0 MFMAs, then the
+        // stage loads (strictly after every read), then the remaining MFMAs
+        {
+            constexpr int RPM = (RD + MF - 1) / MF;            // reads per MFMA
+            constexpr int NRM = (RD + RPM - 1) / RPM;          // MFMAs carrying reads
+            constexpr int LPM = (LD + (MF - NRM) - 1) / (MF - NRM > 0 ? MF - NRM : 1);
+#pragma unroll
+            for (int i = 0; i < NRM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS read
+            }
+#pragma unroll
+            for (int i = 0; i < (LD + LPM - 1) / LPM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, LPM, 0);  // VMEM read (global -> LDS)
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        read_frags(nxt, 0, f0);
+        mma(f1, TM * TN - TAIL, TM * TN);
+        {
+            constexpr int RPT = (RD + MF_TAIL - 1) / MF_TAIL;
+#pragma unroll
+            for (int i = 0; i < MF_TAIL; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, RPT, 0);  // DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // Split-K: wave groups 1..KS-1 hand their partial sums to group 0 via LDS.
@@ -142,12 +211,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
 
     // Epilogue: the per-tensor (or per-expert) scale applied once to the sum.
     const float scale = p.scale_a[t.expert] * p.scale_b[t.expert];
-#pragma unroll
-    for (int mi = 0; mi < C::TM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < C::TN; ++ni)
-            store_block<BF16>(p.C, acc[mi][ni], scale, t.m0 + wm * C::WTM + mi * 32, t.n0 + wn * C::WTN + ni * 32,
-                              t.M, N, t.c_row0, lane);
+    store_tile<BF16>(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane);
 }
 
 template <int BM, int BN, int WM, int WN, int KS, int GROUP_M>

@@ -60,13 +60,12 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_blockscaled_kernel(GemmArgs
     const int b_krow0 = h * 16 + ((lane & 15) >> 1);
     const int b_col0 = wn * C::WTN + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 
-    if (nsteps > 0) load_stage<BM, BN, WM, WN, 1>(t, N, K, 0, lds, wave, lane);
+    const StageLoader<BM, BN, WM, WN, 1> loader(t, N, K, wave, lane);
+    if (nsteps > 0) loader.issue(0, lds);
     for (int step = 0; step < nsteps; ++step) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (step + 1 < nsteps)
-            load_stage<BM, BN, WM, WN, 1>(t, N, K, (int64_t)(step + 1) * BK, lds + ((step + 1) & 1) * C::STAGE, wave,
-                                          lane);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's stage loads have landed in LDS
+        __syncthreads();                // ... and every wave's; the other buffer is free
+        if (step + 1 < nsteps) loader.issue((int64_t)(step + 1) * BK, lds + ((step + 1) & 1) * C::STAGE);
         const lds_u8* As = lds + (step & 1) * C::STAGE;
         const lds_u8* Bs = As + C::A_STAGE;
 #pragma unroll
@@ -110,12 +109,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_blockscaled_kernel(GemmArgs
         }
     }
 
-#pragma unroll
-    for (int mi = 0; mi < C::TM; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < C::TN; ++ni)
-            store_block<BF16>(p.C, acc[mi][ni], 1.0f, t.m0 + wm * C::WTM + mi * 32, t.n0 + wn * C::WTN + ni * 32, M,
-                              N, 0, lane);
+    store_tile<BF16>(p.C, acc, 1.0f, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, M, N, 0, lane);
 }
 
 }  // namespace

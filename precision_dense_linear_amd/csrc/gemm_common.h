@@ -128,60 +128,103 @@ __device__ __forceinline__ TileSlice resolve_tile(const GemmArgs& p) {
     return s;
 }
 
-// Enqueue one stage (KS*128 bytes of K starting at k0) into LDS buffer `dst`.
-// Called by every wave of the workgroup with its wave index; each wave issues
-// A_INSTR/NW + B_INSTR/NW wave-wide 1 KiB loads.
+// Global -> LDS stage loader.  Every wave issues A_INSTR/NW + B_INSTR/NW
+// wave-wide 1 KiB buffer loads per stage.  The per-lane offsets inside a
+// stage do not change from step to step (the buffer resource's base moves
+// instead), so they are computed once:
+//  * A: slot s of a stage -> (K sub-tile, row, chunk position); the global
+//    chunk is the position XOR-swizzled by the row.  Rows beyond the
+//    problem get the out-of-range offset; a K tail (only in the last step
+//    when K is not a multiple of the step) is masked per load.
+//  * B: slot s -> (sub-tile, K-row, position); columns beyond N get the
+//    out-of-range offset.  The K tail needs no mask: the resource covers
+//    only the (K - k0) remaining rows, so later rows read as zero.
 template <int BM, int BN, int WM, int WN, int KS>
-__device__ __forceinline__ void load_stage(const TileSlice& t, int64_t N, int64_t K, int64_t k0, lds_u8* dst,
-                                           int wave, int lane) {
+struct StageLoader {
     using C = TileCfg<BM, BN, WM, WN, KS>;
-    lds_u8* As = dst;
-    lds_u8* Bs = dst + C::A_STAGE;
-    const int64_t rows_here = t.M - t.m0;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(t.A + t.m0 * K + k0, clamp_records(rows_here * K - k0));
-#pragma unroll
-    for (int i = 0; i < C::A_INSTR / C::NW; ++i) {
-        const int q = i * C::NW + wave;
-        const int slot = q * 64 + lane;
-        const int sub = slot / (BM * 8);
-        const int s2 = slot % (BM * 8);
-        const int row = s2 >> 3;
-        const int c = swz_a(row, s2 & 7);
-        const int64_t kk = (int64_t)sub * BK + c * 16;
-        const bool ok = (row < rows_here) && (k0 + kk < K);
-        load16_to_lds(ra, As + q * 1024, ok ? (uint32_t)(row * K + kk) : OOB);
-    }
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.B + k0 * N + t.n0, clamp_records((K - k0) * N - t.n0));
-#pragma unroll
-    for (int i = 0; i < C::B_INSTR / C::NW; ++i) {
-        const int q = i * C::NW + wave;
-        const int slot = q * 64 + lane;
-        const int sub = slot / (BK * BN / 16);
-        const int s2 = slot % (BK * BN / 16);
-        const int r = s2 / (BN / 16);
-        const int c = swz_b<BN>(r, s2 % (BN / 16));
-        const int64_t kr = (int64_t)sub * BK + r;
-        const bool ok = (k0 + kr < K) && (t.n0 + c * 16 < N);
-        load16_to_lds(rb, Bs + q * 1024, ok ? (uint32_t)(kr * N + c * 16) : OOB);
-    }
-}
+    static constexpr int NA = C::A_INSTR / C::NW, NB = C::B_INSTR / C::NW;
+    uint32_t a_off[NA], b_off[NB];
+    uint32_t a_kk[NA];  // K offset of each A chunk inside the stage
+    const uint8_t* a_base;
+    const uint8_t* b_base;
+    int64_t a_bytes, b_bytes;  // bytes from the bases to the end of each operand
+    int64_t K, N;
+    int wave;
 
-// Store one 32x32 accumulator block (rows m_base.., columns n_base.. of the
-// problem), multiplied by `scale`, masking rows >= M and columns >= N.
-template <bool BF16>
-__device__ __forceinline__ void store_block(void* C, const v16f& acc, float scale, int64_t m_base, int64_t n_base,
-                                            int64_t M, int64_t N, int64_t c_row0, int lane) {
-    const int64_t col = n_base + (lane & 31);
-    if (col >= N) return;
+    __device__ __forceinline__ StageLoader(const TileSlice& t, int64_t N_, int64_t K_, int wave_, int lane) {
+        K = K_;
+        N = N_;
+        wave = wave_;
+        const int64_t rows_here = t.M - t.m0;
+        a_base = t.A + t.m0 * K;
+        a_bytes = rows_here * K;
+        b_base = t.B + t.n0;
+        b_bytes = K * N - t.n0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int64_t row = m_base + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= M) continue;
-        const float v = acc[r] * scale;
-        const int64_t idx = (c_row0 + row) * N + col;
-        if constexpr (BF16) reinterpret_cast<uint16_t*>(C)[idx] = f32_to_bf16_rne(v);
-        else reinterpret_cast<float*>(C)[idx] = v;
+        for (int i = 0; i < NA; ++i) {
+            const int slot = (i * C::NW + wave) * 64 + lane;
+            const int sub = slot / (BM * 8);
+            const int s2 = slot % (BM * 8);
+            const int row = s2 >> 3;
+            const int kk = sub * BK + swz_a(row, s2 & 7) * 16;
+            a_kk[i] = kk;
+            a_off[i] = row < rows_here ? (uint32_t)(row * K + kk) : OOB;
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int slot = (i * C::NW + wave) * 64 + lane;
+            const int sub = slot / (BK * BN / 16);
+            const int s2 = slot % (BK * BN / 16);
+            const int r = s2 / (BN / 16);
+            const int c = swz_b<BN>(r, s2 % (BN / 16));
+            b_off[i] = (t.n0 + c * 16 < N) ? (uint32_t)((sub * BK + r) * N + c * 16) : OOB;
+        }
     }
+
+    // Enqueue the stage holding K bytes [k0, k0 + KS*128) into LDS at dst.
+    // Branch-free: past the end of K the resources are empty (every load reads
+    // zero), and the K-tail mask is a select.
+    __device__ __forceinline__ void issue(int64_t k0, lds_u8* dst) const {
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + k0, clamp_records(a_bytes - k0));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + k0 * N, clamp_records(b_bytes - k0 * N));
+        const int64_t krem = K - k0;
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+            load16_to_lds(ra, dst + (i * C::NW + wave) * 1024, (int64_t)a_kk[i] < krem ? a_off[i] : OOB);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) load16_to_lds(rb, dst + C::A_STAGE + (i * C::NW + wave) * 1024, b_off[i]);
+    }
+};
+
+// Store the wave's TM x TN accumulator blocks, multiplied by `scale`: block
+// (mi, ni) covers problem rows m_base + 32mi .. and columns n_base + 32ni ..
+// Addresses are 32-bit offsets from one wave-uniform base; rows >= M and
+// columns >= N are masked only when the wave tile crosses an edge.
+template <bool BF16, int TM, int TN>
+__device__ __forceinline__ void store_tile(void* C, const v16f (&acc)[TM][TN], float scale, int64_t m_base,
+                                           int64_t n_base, int64_t M, int64_t N, int64_t c_row0, int lane) {
+    constexpr int OSZ = BF16 ? 2 : 4;
+    uint8_t* base = reinterpret_cast<uint8_t*>(C) + ((c_row0 + m_base) * N + n_base) * OSZ;
+    const bool full = (m_base + 32 * TM <= M) && (n_base + 32 * TN <= N);
+    const int rows_left = (int)(M - m_base < 32 * TM ? M - m_base : 32 * TM);
+    const int cols_left = (int)(N - n_base < 32 * TN ? N - n_base : 32 * TN);
+    const int ldc = (int)N * OSZ;
+#pragma unroll
+    for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < TN; ++ni) {
+            const int col = ni * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const float v = acc[mi][ni][r] * scale;
+                if (full || (row < rows_left && col < cols_left)) {
+                    uint8_t* dst = base + row * ldc + col * OSZ;
+                    if constexpr (BF16) *reinterpret_cast<__bf16*>(dst) = (__bf16)v;  // RNE (v_cvt_pk_bf16_f32)
+                    else *reinterpret_cast<float*>(dst) = v;
+                }
+            }
+        }
 }
 
 }  // namespace fp8k

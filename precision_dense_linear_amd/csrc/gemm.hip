@@ -35,7 +35,9 @@ template <int BM, int BN, int WM, int WN, int KS, int GROUP_M, bool BF16, bool E
 __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     using C = TileCfg<BM, BN, WM, WN, KS>;
     constexpr int TM = C::TM, TN = C::TN;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+    constexpr int EPI = (KS > 1 ? C::RED : 0) + WM * WN * TileStore<BF16, TM, TN>::LDS_BYTES;
+    static_assert(EPI <= 160 * 1024, "epilogue LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS > EPI ? C::LDS : EPI];
 
     const TileSlice t = resolve_tile<BM, BN, GROUP_M>(p);
     if (!t.valid) return;
@@ -108,10 +110,10 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
                 // (K 32*(l/32) + 8c .. +7) feeds the c-th, for A and B alike
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    acc[mi][ni] = mfma_32x32x16_bf16(e4m3x8_to_bf16(f.a[mi][2 * c], f.a[mi][2 * c + 1]),
-                                                     e4m3x8_to_bf16(f.b[ni][2 * c], f.b[ni][2 * c + 1]), acc[mi][ni]);
+                    acc[mi][ni] = mfma_32x32x16_bf16(e4m3x8_to_bf16(f.b[ni][2 * c], f.b[ni][2 * c + 1]),
+                                                     e4m3x8_to_bf16(f.a[mi][2 * c], f.a[mi][2 * c + 1]), acc[mi][ni]);
             } else {
-                acc[mi][ni] = mfma_32x32x64_e4m3(f.a[mi], f.b[ni], acc[mi][ni]);
+                acc[mi][ni] = mfma_32x32x64_e4m3(f.b[ni], f.a[mi], acc[mi][ni]);  // B first: acc holds C^T
             }
         }
     };
@@ -150,9 +152,12 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
         // order: the f1 reads spread over the first slice-0 MFMAs, then the
         // stage loads (strictly after every read), then the remaining MFMAs
         {
-            constexpr int RPM = (RD + MF - 1) / MF;            // reads per MFMA
+            // reads over the first few MFMAs, then the loads: early, so that
+            // the loads have most of the step to land before the barrier
+            constexpr int NR0 = MF < 6 ? MF : 6;
+            constexpr int RPM = (RD + NR0 - 1) / NR0;          // reads per MFMA
             constexpr int NRM = (RD + RPM - 1) / RPM;          // MFMAs carrying reads
-            constexpr int LPM = (LD + (MF - NRM) - 1) / (MF - NRM > 0 ? MF - NRM : 1);
+            constexpr int LPM = (MF - NRM) >= 4 ? (LD + 3) / 4 : (LD + (MF - NRM) - 1) / (MF - NRM > 0 ? MF - NRM : 1);
 #pragma unroll
             for (int i = 0; i < NRM; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
@@ -210,8 +215,13 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     }
 
     // Epilogue: the per-tensor (or per-expert) scale applied once to the sum.
+    // With KS > 1 the LDS scratch sits after the reduction buffer; otherwise
+    // every wave must first be done with the stage buffers.
+    if constexpr (KS == 1) __syncthreads();
+    using Store = TileStore<BF16, TM, TN>;
+    lds_u8* scratch = lds + (KS > 1 ? C::RED : 0) + (wm * WN + wn) * Store::LDS_BYTES;
     const float scale = p.scale_a[t.expert] * p.scale_b[t.expert];
-    store_tile<BF16>(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane);
+    Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch);
 }
 
 template <int BM, int BN, int WM, int WN, int KS, int GROUP_M>

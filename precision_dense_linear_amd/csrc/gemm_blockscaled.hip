@@ -100,8 +100,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_blockscaled_kernel(GemmArgs
                     if (cb[ni] * 32 >= N) continue;
                     const float s = sa * p.scale_b[kbg * NB + cb[ni]];
                     v16f part = {};
-                    part = mfma_32x32x16_bf16(a_lo[mi], b0[ni], part);
-                    part = mfma_32x32x16_bf16(a_hi[mi], b1[ni], part);
+                    part = mfma_32x32x16_bf16(b0[ni], a_lo[mi], part);  // B first: C^T layout
+                    part = mfma_32x32x16_bf16(b1[ni], a_hi[mi], part);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[mi][ni][r] = fmaf(s, part[r], acc[mi][ni][r]);
                 }
@@ -109,7 +109,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_blockscaled_kernel(GemmArgs
         }
     }
 
-    store_tile<BF16>(p.C, acc, 1.0f, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, M, N, 0, lane);
+    __syncthreads();  // every wave is done with the stage buffers
+    using Store = TileStore<BF16, C::TM, C::TN>;
+    Store::run(p.C, acc, 1.0f, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, M, N, 0, lane,
+               lds + (wm * WN + wn) * Store::LDS_BYTES);
 }
 
 }  // namespace

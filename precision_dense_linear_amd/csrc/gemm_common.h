@@ -196,35 +196,72 @@ struct StageLoader {
     }
 };
 
-// Store the wave's TM x TN accumulator blocks, multiplied by `scale`: block
-// (mi, ni) covers problem rows m_base + 32mi .. and columns n_base + 32ni ..
-// Addresses are 32-bit offsets from one wave-uniform base; rows >= M and
-// columns >= N are masked only when the wave tile crosses an edge.
+// Epilogue: store the wave's TM x TN accumulator blocks, multiplied by
+// `scale`.  The kernels issue each MFMA with the B fragment as the first
+// operand, so accumulator block (mi, ni) holds C^T: element r of lane l is
+// row 32mi + (l & 31), column 32ni + 8(r >> 2) + 4(l >> 5) + (r & 3) of the
+// wave tile -- four consecutive columns of one row per r/4 group.  Those go
+// to a wave-private LDS region as 8-byte (BF16) or 16-byte (FP32) writes,
+// row-major with the 16-byte chunks XOR-swizzled by row, and come back as
+// 16-byte row chunks that are stored to C fully coalesced (one 1 KiB
+// contiguous run per 64 lanes and instruction).  Rows are done in passes of
+// at most 32 KiB of LDS.  Rows >= M and columns >= N (N % 16 == 0, so a
+// chunk is either inside or outside) are masked only at the edges.
 template <bool BF16, int TM, int TN>
-__device__ __forceinline__ void store_tile(void* C, const v16f (&acc)[TM][TN], float scale, int64_t m_base,
-                                           int64_t n_base, int64_t M, int64_t N, int64_t c_row0, int lane) {
-    constexpr int OSZ = BF16 ? 2 : 4;
-    uint8_t* base = reinterpret_cast<uint8_t*>(C) + ((c_row0 + m_base) * N + n_base) * OSZ;
-    const bool full = (m_base + 32 * TM <= M) && (n_base + 32 * TN <= N);
-    const int rows_left = (int)(M - m_base < 32 * TM ? M - m_base : 32 * TM);
-    const int cols_left = (int)(N - n_base < 32 * TN ? N - n_base : 32 * TN);
-    const int ldc = (int)N * OSZ;
+struct TileStore {
+    static constexpr int OSZ = BF16 ? 2 : 4;
+    static constexpr int ROWB = 32 * TN * OSZ;  // bytes per wave-tile row
+    static constexpr int CHUNKS = ROWB / 16;
+    static constexpr int PASS_MI = (32768 / (32 * ROWB)) < TM ? (32768 / (32 * ROWB)) : TM;
+    static constexpr int LDS_BYTES = PASS_MI * 32 * ROWB;  // per wave
+    static_assert(PASS_MI >= 1 && TM % PASS_MI == 0, "epilogue pass size");
+
+    __device__ static __forceinline__ int swz(int row, int ch) { return ch ^ (row & (CHUNKS - 1)); }
+
+    __device__ static __forceinline__ void run(void* C, const v16f (&acc)[TM][TN], float scale, int64_t m_base,
+                                               int64_t n_base, int64_t M, int64_t N, int64_t c_row0, int lane,
+                                               lds_u8* scratch) {
+        const bool full = (m_base + 32 * TM <= M) && (n_base + 32 * TN <= N);
+        const int rows_left = (int)(M - m_base < 32 * TM ? M - m_base : 32 * TM);
+        const int cols_left = (int)(N - n_base < 32 * TN ? N - n_base : 32 * TN);
+        uint8_t* base = reinterpret_cast<uint8_t*>(C) + ((c_row0 + m_base) * N + n_base) * OSZ;
+        const int ldc = (int)N * OSZ;
 #pragma unroll
-    for (int mi = 0; mi < TM; ++mi)
+        for (int p0 = 0; p0 < TM; p0 += PASS_MI) {
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni) {
-            const int col = ni * 32 + (lane & 31);
+            for (int mi = 0; mi < PASS_MI; ++mi) {
+                const int row = mi * 32 + (lane & 31);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const float v = acc[mi][ni][r] * scale;
-                if (full || (row < rows_left && col < cols_left)) {
-                    uint8_t* dst = base + row * ldc + col * OSZ;
-                    if constexpr (BF16) *reinterpret_cast<__bf16*>(dst) = (__bf16)v;  // RNE (v_cvt_pk_bf16_f32)
-                    else *reinterpret_cast<float*>(dst) = v;
-                }
+                for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const v16f& a = acc[p0 + mi][ni];
+                        const int cb = (ni * 32 + 8 * q + 4 * (lane >> 5)) * OSZ;  // byte column in the row
+                        lds_u8* dst = scratch + row * ROWB + swz(row, cb >> 4) * 16 + (cb & 15);
+                        if constexpr (BF16) {
+                            typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+                            const v4bf v = {(__bf16)(a[4 * q] * scale), (__bf16)(a[4 * q + 1] * scale),
+                                            (__bf16)(a[4 * q + 2] * scale), (__bf16)(a[4 * q + 3] * scale)};
+                            *(__attribute__((address_space(3))) v4bf*)dst = v;
+                        } else {
+                            const v4f v = {a[4 * q] * scale, a[4 * q + 1] * scale, a[4 * q + 2] * scale,
+                                           a[4 * q + 3] * scale};
+                            *(__attribute__((address_space(3))) v4f*)dst = v;
+                        }
+                    }
+            }
+            constexpr int ITER = PASS_MI * 32 * CHUNKS / 64;
+#pragma unroll
+            for (int it = 0; it < ITER; ++it) {
+                const int idx = it * 64 + lane;
+                const int row = idx / CHUNKS, ch = idx % CHUNKS;
+                const v4i v = lds_read16(scratch + row * ROWB + swz(row, ch) * 16);
+                const int grow = p0 * 32 + row, gcolb = ch * 16;
+                if (full || (grow < rows_left && gcolb < cols_left * OSZ))
+                    *reinterpret_cast<v4i*>(base + grow * ldc + gcolb) = v;
             }
         }
-}
+    }
+};
 
 }  // namespace fp8k

@@ -28,7 +28,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (published; 256 CU x 8192 flop/clk x 2.4 GHz = 5033)
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA (published)
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def csrc_sha256():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "precision_dense_linear_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed rocprofv3 byte counters, if
+    they were taken on the kernel sources as they are now (else None)."""
+    path = os.path.join(PROFILES, {"gemm8192": "gemm_kernel_8192x8192x8192_bf16.traffic.json"}.get(workload, "-"))
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    return rec["traffic_bytes"] if rec.get("csrc_sha256") == csrc_sha256() else None
 
 
 def parse():
@@ -40,6 +62,10 @@ def parse():
                     choices=["gemm8192", "gemm1024", "gemm256", "llm16", "llm128", "llm4096", "blockscaled8192",
                              "moe"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy twice (reference for the HBM byte counters)")
+    ap.add_argument("--warmup-seconds", type=float, default=0.3,
+                    help="keep warming up at least this long so clocks have settled")
     ap.add_argument("--cpu-rows", type=int, default=768, help="rows of A in the oracle's timed sample")
     return ap.parse_args()
 
@@ -171,11 +197,24 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(2):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4}))
+        return
     w = Workload(args.workload, dev)
     stream = torch.cuda.current_stream(dev)
 
-    for _ in range(args.warmup):
+    t_w = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
         w.step()
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # Timed region: K whole steps; GEMM launches bracketed by events on the
@@ -223,12 +262,15 @@ def main():
     gemm_tflops = w.flops / (avg_gemm_ms * 1e-3) / 1e12
     mfma_bound = w.flops / w.gemm_bytes() > FP8_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3
     if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None}
+        # the default (exact-product) kernels multiply on the BF16 matrix cores
+        peak = BF16_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / peak, 4), "traffic": measured_traffic(args.workload),
+                "peak_basis": "dense BF16 MFMA: E4M3 operands are widened exactly to BF16 so every product is exact"}
     else:
         gbps = w.gemm_bytes() / (avg_gemm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args.workload)}
     roof["kernel"] = "gemm_kernel (fp8_gemm)" if w.kind == "pertensor" else (
         "gemm_blockscaled_kernel" if w.kind == "block" else "gemm_kernel (fp8_grouped_gemm)")
     roof["avg_kernel_us"] = round(avg_gemm_ms * 1e3, 2)

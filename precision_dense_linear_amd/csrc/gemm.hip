@@ -31,9 +31,9 @@ struct Frags {
     v8i b[TN];
 };
 
-template <int BM, int BN, int WM, int WN, int KS, int GROUP_M, bool BF16, bool EXACT>
+template <int BM, int BN, int WM, int WN, int KS, int NBUF, int GROUP_M, bool BF16, bool EXACT>
 __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
-    using C = TileCfg<BM, BN, WM, WN, KS>;
+    using C = PipeCfg<BM, BN, WM, WN, KS, NBUF>;
     constexpr int TM = C::TM, TN = C::TN;
     constexpr int EPI = (KS > 1 ? C::RED : 0) + WM * WN * TileStore<BF16, TM, TN>::LDS_BYTES;
     static_assert(EPI <= 160 * 1024, "epilogue LDS budget");
@@ -48,9 +48,9 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     const int wm = (wave % (WM * WN)) / WN;
     const int wn = wave % WN;
     const int64_t K = p.K, N = p.N;
-    const int nsteps = (int)((K + KS * BK - 1) / (KS * BK));
+    const int nsteps = (int)((K + KS * BKP - 1) / (KS * BKP));
     lds_u8* lds = (lds_u8*)smem;
-    const StageLoader<BM, BN, WM, WN, KS> loader(t, N, K, wave, lane);
+    const PipeLoader<BM, BN, WM, WN, KS, NBUF> loader(t, N, K, wave, lane, (uint32_t)(uintptr_t)lds);
 
     v16f acc[TM][TN];
 #pragma unroll
@@ -61,144 +61,122 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // Per-lane LDS byte offsets of this wave's operands inside a stage.
-    int a_off[TM][2];  // [block][64-byte slice]: chunk pair start of row (lane%32)
-    int b_off[TN][2][4];
+    int a_off[TM];
+    int b_off[TN][4];
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
         const int row = wm * C::WTM + mi * 32 + (lane & 31);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) a_off[mi][s] = ks * BM * BK + row * BK + swz_a(row, s * 4 + (lane >> 5) * 2) * 16;
+        a_off[mi] = ks * BM * BKP + row * BKP + swz_a64(row, (lane >> 5) * 2) * 16;
     }
-    // the second chunk of the pair sits at position (c+1) ^ swz = (c ^ swz) ^ 1: i.e. +/-16 bytes
-    const int a_pair = (((lane & 31) >> 1) & 1) ? -16 : 16;
+    // the second chunk of the pair: (2h+1) ^ f = (2h ^ f) ^ 1, i.e. +-16 bytes
+    const int a_pair = (((lane & 31) >> 2) & 1) ? -16 : 16;
 #pragma unroll
     for (int ni = 0; ni < TN; ++ni) {
         const int col = wn * C::WTN + ni * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int tq = 0; tq < 4; ++tq) {
-                const int kr = s * 64 + (lane >> 5) * 32 + ((lane & 15) >> 1) + 8 * tq;
-                b_off[ni][s][tq] = C::A_STAGE + ks * BK * BN + kr * BN + swz_b<BN>(kr, col >> 4) * 16 + (col & 15);
-            }
+        for (int tq = 0; tq < 4; ++tq) {
+            const int kr = (lane >> 5) * 32 + ((lane & 15) >> 1) + 8 * tq;
+            b_off[ni][tq] = C::A_STAGE + ks * BKP * BN + kr * BN + swz_b<BN>(kr, col >> 4) * 16 + (col & 15);
+        }
     }
 
-    auto read_frags = [&](const lds_u8* stage, int s, Frags<TM, TN>& f) {
+    auto read_frags = [&](int st, Frags<TM, TN>& f) {
+        const lds_u8* stage = lds + (st % NBUF) * C::STAGE;
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi) {
-            const v4i lo = lds_read16(stage + a_off[mi][s]);
-            const v4i hi = lds_read16(stage + a_off[mi][s] + a_pair);
+            const v4i lo = lds_read16(stage + a_off[mi]);
+            const v4i hi = lds_read16(stage + a_off[mi] + a_pair);
             f.a[mi] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni) {
             v2i q[4];
 #pragma unroll
-            for (int tq = 0; tq < 4; ++tq) q[tq] = lds_read_tr8(stage + b_off[ni][s][tq]);
+            for (int tq = 0; tq < 4; ++tq) q[tq] = lds_read_tr8(stage + b_off[ni][tq]);
             f.b[ni] = (v8i){q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
         }
     };
 
-    // The MFMAs of one 64-byte slice, blocks [first, last) in (mi, ni) order.
-    auto mma = [&](const Frags<TM, TN>& f, int first, int last) {
+    // All MFMAs of one 64-byte slice.  The B fragment is the first operand, so
+    // accumulator block (mi, ni) holds C^T (see TileStore).
+    auto mma = [&](const Frags<TM, TN>& f) {
 #pragma unroll
-        for (int idx = 0; idx < TM * TN; ++idx) {
-            if (idx < first || idx >= last) continue;
-            const int mi = idx / TN, ni = idx % TN;
-            if constexpr (EXACT) {
-                // four K=16 BF16 MFMAs; chunk c of each lane's 32 bytes
-                // (K 32*(l/32) + 8c .. +7) feeds the c-th, for A and B alike
+        for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    acc[mi][ni] = mfma_32x32x16_bf16(e4m3x8_to_bf16(f.b[ni][2 * c], f.b[ni][2 * c + 1]),
-                                                     e4m3x8_to_bf16(f.a[mi][2 * c], f.a[mi][2 * c + 1]), acc[mi][ni]);
-            } else {
-                acc[mi][ni] = mfma_32x32x64_e4m3(f.b[ni], f.a[mi], acc[mi][ni]);  // B first: acc holds C^T
+            for (int ni = 0; ni < TN; ++ni) {
+                if constexpr (EXACT) {
+                    // four K=16 BF16 MFMAs; chunk c of each lane's 32 bytes
+                    // (K 32*(l/32) + 8c .. +7) feeds the c-th, for A and B alike
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[mi][ni] = mfma_32x32x16_bf16(e4m3x8_to_bf16(f.b[ni][2 * c], f.b[ni][2 * c + 1]),
+                                                         e4m3x8_to_bf16(f.a[mi][2 * c], f.a[mi][2 * c + 1]),
+                                                         acc[mi][ni]);
+                } else {
+                    acc[mi][ni] = mfma_32x32x64_e4m3(f.b[ni], f.a[mi], acc[mi][ni]);
+                }
             }
-        }
     };
 
-    // Pipeline, per 128-byte step k (LDS buffer k&1; fragments f0/f1 for its
-    // two 64-byte slices; f0 was read at the end of step k-1):
-    //   read the slice-1 fragments f1 -- before any new global->LDS load is
-    //   in flight, so these LDS reads need no wait on them;
-    //   issue the global loads of stage k+1 into the other buffer;
-    //   slice-0 MFMAs (f0), then all but the last TAIL slice-1 MFMAs;
-    //   wait for stage k+1 and barrier: it is in LDS, and buffer k&1 is free;
-    //   read stage k+1's slice-0 fragments f0 under the last TAIL MFMAs.
-    // The body is branch-free (past the end of K the loads are empty), and
-    // sched_barrier keeps the compiler from moving MFMAs across the barrier.
-    constexpr int TAIL = (TM * TN) >= 8 ? 4 : ((TM * TN) >= 2 ? (TM * TN) / 2 : 1);
+    // Pipeline: stage s lives in LDS buffer s % NBUF; D = NBUF-1 stages are in
+    // flight.  Iteration s (fragments of slice s already requested):
+    //   wait until stage s+1 has landed (the D-2 newer stages may still be in
+    //   flight), barrier -- stage s+1 is visible to all waves, and every wave
+    //   has finished its MFMAs of slice s-1, hence its reads of buffer
+    //   (s-1) % NBUF = (s+D) % NBUF;
+    //   issue stage s+D into that buffer;
+    //   read the slice s+1 fragments while the slice s MFMAs run.
+    // Loads past the end of K are empty (they read zero), so the body is
+    // branch-free and the in-flight load count is the same every iteration.
+    constexpr int D = NBUF - 1;
+    constexpr int MF = TM * TN * (EXACT ? 4 : 1);  // MFMA instructions per slice
+    constexpr int RD = 2 * TM + 4 * TN;             // LDS reads per slice
     Frags<TM, TN> f0, f1;
-    if (nsteps > 0) {
-        loader.issue(0, lds);
-        __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int st = 0; st < D; ++st) loader.issue(st);
+    wait_vmcnt<(D - 1) * C::LPS>();
+    __syncthreads();
+    read_frags(0, f0);
+
+    auto iteration = [&](int s, Frags<TM, TN>& cur, Frags<TM, TN>& next) {
+        wait_vmcnt<(D - 2) * C::LPS>();
         __syncthreads();
-        read_frags(lds, 0, f0);
-    }
-    // MFMA instructions per 64-byte slice, LDS reads per fragment set, and
-    // global->LDS loads per stage, for the interleave below.
-    constexpr int MF = TM * TN * (EXACT ? 4 : 1);
-    constexpr int MF_TAIL = TAIL * (EXACT ? 4 : 1);
-    constexpr int RD = 2 * TM + 4 * TN;
-    constexpr int LD = StageLoader<BM, BN, WM, WN, KS>::NA + StageLoader<BM, BN, WM, WN, KS>::NB;
-    for (int step = 0; step < nsteps; ++step) {
-        const lds_u8* cur = lds + (step & 1) * C::STAGE;
-        lds_u8* nxt = lds + ((step + 1) & 1) * C::STAGE;
-        read_frags(cur, 1, f1);
-        loader.issue((int64_t)(step + 1) * (KS * BK), nxt);
-        mma(f0, 0, TM * TN);
-        mma(f1, 0, TM * TN - TAIL);
-        // order: the f1 reads spread over the first slice-0 MFMAs, then the
-        // stage loads (strictly after every read), then the remaining MFMAs
-        {
-            // reads over the first few MFMAs, then the loads: early, so that
-            // the loads have most of the step to land before the barrier
-            constexpr int NR0 = MF < 6 ? MF : 6;
-            constexpr int RPM = (RD + NR0 - 1) / NR0;          // reads per MFMA
-            constexpr int NRM = (RD + RPM - 1) / RPM;          // MFMAs carrying reads
-            constexpr int LPM = (MF - NRM) >= 4 ? (LD + 3) / 4 : (LD + (MF - NRM) - 1) / (MF - NRM > 0 ? MF - NRM : 1);
+        loader.issue(s + D);
+        read_frags(s + 1, next);
+        mma(cur);
+        // interleave: the next fragment's LDS reads spread over the MFMAs
+        constexpr int RPM = (RD + MF - 1) / MF;
 #pragma unroll
-            for (int i = 0; i < NRM; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS read
-            }
-#pragma unroll
-            for (int i = 0; i < (LD + LPM - 1) / LPM; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, LPM, 0);  // VMEM read (global -> LDS)
-            }
+        for (int i = 0; i < (RD + RPM - 1) / RPM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
         }
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        read_frags(nxt, 0, f0);
-        mma(f1, TM * TN - TAIL, TM * TN);
-        {
-            constexpr int RPT = (RD + MF_TAIL - 1) / MF_TAIL;
-#pragma unroll
-            for (int i = 0; i < MF_TAIL; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, RPT, 0);  // DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+        iteration(s, f0, f1);
+        iteration(s + 1, f1, f0);
     }
+    if (s < nsteps) iteration(s, f0, f1);
+
+    // Drain: the empty tail loads must land before the LDS is reused.
+    wait_vmcnt<0>();
 
     // Split-K: wave groups 1..KS-1 hand their partial sums to group 0 via LDS.
     if constexpr (KS > 1) {
         __syncthreads();
         float* red = (float*)smem;
         const int wslot = wm * WN + wn;
-        constexpr int PER = C::TM * C::TN * 16 * 64;
+        constexpr int PER = TM * TN * 16 * 64;
         if (ks > 0) {
             float* dst = red + ((ks - 1) * WM * WN + wslot) * PER;
 #pragma unroll
-            for (int mi = 0; mi < C::TM; ++mi)
+            for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < C::TN; ++ni)
+                for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) dst[((mi * C::TN + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
+                    for (int r = 0; r < 16; ++r) dst[((mi * TN + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
         }
         __syncthreads();
         if (ks > 0) return;
@@ -206,11 +184,11 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
         for (int g = 0; g < KS - 1; ++g) {
             const float* src = red + (g * WM * WN + wslot) * PER;
 #pragma unroll
-            for (int mi = 0; mi < C::TM; ++mi)
+            for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < C::TN; ++ni)
+                for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[mi][ni][r] += src[((mi * C::TN + ni) * 16 + r) * 64 + lane];
+                    for (int r = 0; r < 16; ++r) acc[mi][ni][r] += src[((mi * TN + ni) * 16 + r) * 64 + lane];
         }
     }
 
@@ -224,7 +202,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch);
 }
 
-template <int BM, int BN, int WM, int WN, int KS, int GROUP_M>
+template <int BM, int BN, int WM, int WN, int KS, int NBUF, int GROUP_M>
 hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
     GemmArgs a;
     a.A = g.A;
@@ -246,11 +224,11 @@ hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
     constexpr int NT = 64 * WM * WN * KS;
     const dim3 grid((unsigned)blocks), block(NT);
     if (g.fast_acc) {
-        if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, true, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, false, false>), grid, block, 0, s, a);
+        if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NBUF, GROUP_M, true, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NBUF, GROUP_M, false, false>), grid, block, 0, s, a);
     } else {
-        if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, false, true>), grid, block, 0, s, a);
+        if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NBUF, GROUP_M, true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NBUF, GROUP_M, false, true>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -264,9 +242,9 @@ hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
 //  * larger M: 256 x 256 tiles, 4 waves of 128 x 128 -- MFMA bound.
 hipError_t launch_gemm(const GemmProblem& g, hipStream_t s) {
     const int64_t rows_per_problem = g.experts ? (g.M + g.experts - 1) / g.experts : g.M;
-    if (rows_per_problem <= 64) return launch_cfg<32, 64, 1, 2, 2, 8>(g, s);
-    if (rows_per_problem <= 1024) return launch_cfg<128, 128, 2, 2, 1, 8>(g, s);
-    return launch_cfg<256, 256, 2, 2, 1, 8>(g, s);
+    if (rows_per_problem <= 64) return launch_cfg<32, 64, 1, 2, 2, 4, 8>(g, s);
+    if (rows_per_problem <= 1024) return launch_cfg<128, 128, 2, 2, 1, 4, 8>(g, s);
+    return launch_cfg<256, 256, 2, 2, 1, 4, 8>(g, s);
 }
 
 }  // namespace fp8k

@@ -196,6 +196,116 @@ struct StageLoader {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Deep pipeline (per-tensor and grouped GEMM): stages of 64 bytes of K per
+// wave group, NBUF stage buffers in LDS, NBUF-1 stages in flight.
+//  * A stage: KS sub-tiles of [BM rows][64 bytes]; chunk c of row r sits at
+//    position c ^ ((r >> 2) & 3), so the 16 rows of one ds_read_b128 phase
+//    (four rows per 256-byte bank window) hit 16 distinct chunks.
+//  * B stage: KS sub-tiles of [64 K-rows][BN bytes], swizzled as swz_b.
+// ---------------------------------------------------------------------------
+constexpr int BKP = 64;  // bytes of K per wave group per pipelined stage
+
+__device__ __forceinline__ int swz_a64(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+template <int BM, int BN, int WM, int WN, int KS, int NBUF>
+struct PipeCfg {
+    static constexpr int NW = WM * WN * KS;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static constexpr int A_STAGE = KS * BM * BKP;
+    static constexpr int B_STAGE = KS * BKP * BN;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int A_INSTR = A_STAGE / 1024;
+    static constexpr int B_INSTR = B_STAGE / 1024;
+    static constexpr int NA = A_INSTR / NW, NB = B_INSTR / NW;
+    static constexpr int LPS = NA + NB;  // global->LDS loads per wave per stage
+    static constexpr int RED = (KS > 1) ? (KS - 1) * BM * BN * 4 : 0;
+    static constexpr int LDS = NBUF * STAGE;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "stage loads must split evenly over waves");
+    static_assert(BN >= 64 && BN <= 256 && (BN & (BN - 1)) == 0, "BN must be 64, 128 or 256");
+    static_assert(NBUF >= 3 && (NBUF - 3) * LPS <= 63, "in-flight loads must fit the vmcnt counter");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// One wave-wide global->LDS load, written as inline assembly: M0 holds the
+// wave's LDS destination, lane l's 16 bytes land at M0 + 16*l.  The compiler
+// does not see these as LDS writes, so it neither serialises later LDS reads
+// behind them nor counts them; the kernel waits for them explicitly with
+// s_waitcnt vmcnt(n), n = loads issued after the stage it needs.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14, expcnt 6:4 = 7,
+// lgkmcnt 11:8 = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int WM, int WN, int KS, int NBUF>
+struct PipeLoader {
+    using C = PipeCfg<BM, BN, WM, WN, KS, NBUF>;
+    uint32_t a_off[C::NA], a_kk[C::NA], b_off[C::NB];
+    const uint8_t* a_base;
+    const uint8_t* b_base;
+    int64_t a_bytes, b_bytes, K, N;
+    uint32_t lds_wave;  // LDS byte address of this wave's first 1 KiB slot in buffer 0
+
+    __device__ __forceinline__ PipeLoader(const TileSlice& t, int64_t N_, int64_t K_, int wave, int lane,
+                                          uint32_t lds_base) {
+        K = K_;
+        N = N_;
+        const int64_t rows_here = t.M - t.m0;
+        a_base = t.A + t.m0 * K;
+        a_bytes = rows_here * K;
+        b_base = t.B + t.n0;
+        b_bytes = K * N - t.n0;
+        lds_wave = lds_base + wave * 1024;
+#pragma unroll
+        for (int i = 0; i < C::NA; ++i) {
+            const int slot = (i * C::NW + wave) * 64 + lane;
+            const int sub = slot / (BM * 4);
+            const int s2 = slot % (BM * 4);
+            const int row = s2 >> 2;
+            const int kk = sub * BKP + swz_a64(row, s2 & 3) * 16;
+            a_kk[i] = kk;
+            a_off[i] = row < rows_here ? (uint32_t)(row * K + kk) : OOB;
+        }
+#pragma unroll
+        for (int i = 0; i < C::NB; ++i) {
+            const int slot = (i * C::NW + wave) * 64 + lane;
+            const int sub = slot / (BKP * BN / 16);
+            const int s2 = slot % (BKP * BN / 16);
+            const int r = s2 / (BN / 16);
+            const int c = swz_b<BN>(r, s2 % (BN / 16));
+            b_off[i] = (t.n0 + c * 16 < N) ? (uint32_t)((sub * BKP + r) * N + c * 16) : OOB;
+        }
+    }
+
+    // Stage `st` (K bytes [st*KS*64, +KS*64)) into LDS buffer st % NBUF.  Past
+    // the end of K the resources are empty, so every load reads zero.
+    __device__ __forceinline__ void issue(int st) const {
+        const int64_t k0 = (int64_t)st * (KS * BKP);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + k0, clamp_records(a_bytes - k0));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + k0 * N, clamp_records(b_bytes - k0 * N));
+        const int64_t krem = K - k0;
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_wave + (uint32_t)(st % NBUF) * C::STAGE);
+#pragma unroll
+        for (int i = 0; i < C::NA; ++i)
+            dma16(ra, dst + i * C::NW * 1024, (int64_t)a_kk[i] < krem ? a_off[i] : OOB);
+#pragma unroll
+        for (int i = 0; i < C::NB; ++i) dma16(rb, dst + C::A_STAGE + i * C::NW * 1024, b_off[i]);
+    }
+};
+
 // Epilogue: store the wave's TM x TN accumulator blocks, multiplied by
 // `scale`.  The kernels issue each MFMA with the B fragment as the first
 // operand, so accumulator block (mi, ni) holds C^T: element r of lane l is

@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy twice (reference for the HBM byte counters)")
-    ap.add_argument("--warmup-seconds", type=float, default=0.3,
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="keep warming up at least this long so clocks have settled")
     ap.add_argument("--cpu-rows", type=int, default=768, help="rows of A in the oracle's timed sample")
     return ap.parse_args()

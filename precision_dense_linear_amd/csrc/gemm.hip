@@ -100,22 +100,30 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     // All MFMAs of one 64-byte slice.  The B fragment is the first operand, so
     // accumulator block (mi, ni) holds C^T (see TileStore).
     auto mma = [&](const Frags<TM, TN>& f) {
+        if constexpr (EXACT) {
+            // four K=16 BF16 MFMAs per block; chunk c of each lane's 32 bytes
+            // (K 32*(l/32) + 8c .. +7) feeds the c-th, for A and B alike.  The
+            // chunk loop is outermost, so consecutive MFMAs update different
+            // accumulators and the conversions of chunk c+1 can overlap the
+            // MFMAs of chunk c.
 #pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
+            for (int c = 0; c < 4; ++c) {
+                v8bf ab[TM], bb[TN];
 #pragma unroll
-            for (int ni = 0; ni < TN; ++ni) {
-                if constexpr (EXACT) {
-                    // four K=16 BF16 MFMAs; chunk c of each lane's 32 bytes
-                    // (K 32*(l/32) + 8c .. +7) feeds the c-th, for A and B alike
+                for (int mi = 0; mi < TM; ++mi) ab[mi] = e4m3x8_to_bf16(f.a[mi][2 * c], f.a[mi][2 * c + 1]);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        acc[mi][ni] = mfma_32x32x16_bf16(e4m3x8_to_bf16(f.b[ni][2 * c], f.b[ni][2 * c + 1]),
-                                                         e4m3x8_to_bf16(f.a[mi][2 * c], f.a[mi][2 * c + 1]),
-                                                         acc[mi][ni]);
-                } else {
-                    acc[mi][ni] = mfma_32x32x64_e4m3(f.b[ni], f.a[mi], acc[mi][ni]);
-                }
+                for (int ni = 0; ni < TN; ++ni) bb[ni] = e4m3x8_to_bf16(f.b[ni][2 * c], f.b[ni][2 * c + 1]);
+#pragma unroll
+                for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < TN; ++ni) acc[mi][ni] = mfma_32x32x16_bf16(bb[ni], ab[mi], acc[mi][ni]);
             }
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < TN; ++ni) acc[mi][ni] = mfma_32x32x64_e4m3(f.b[ni], f.a[mi], acc[mi][ni]);
+        }
     };
 
     // Pipeline: stage s lives in LDS buffer s % NBUF; D = NBUF-1 stages are in

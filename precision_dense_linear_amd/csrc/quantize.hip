@@ -37,23 +37,48 @@ __device__ __forceinline__ void block_max_to(float m, float* dst) {
     }
 }
 
-// amax over n floats (x 16-byte aligned); grid-stride over v4fs.
+// amax over n floats (x 16-byte aligned).  Grid-stride over groups of U
+// float4s per thread (U independent 16-byte loads in flight per thread).
+constexpr int AMAX_U = 8;
 __global__ void __launch_bounds__(kThreads) amax_kernel(const float* __restrict__ x, int64_t n, float* amax) {
     const int64_t n4 = n >> 2;
     const v4f* x4 = reinterpret_cast<const v4f*>(x);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     float m = 0.0f;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-        v4f v = __builtin_nontemporal_load(&x4[i]);
+    int64_t i = tid;
+    for (; i + (AMAX_U - 1) * stride < n4; i += AMAX_U * stride) {
+        v4f v[AMAX_U];
+#pragma unroll
+        for (int u = 0; u < AMAX_U; ++u) v[u] = x4[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < AMAX_U; ++u)
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
+    }
+    for (; i < n4; i += stride) {
+        const v4f v = x4[i];
         m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
-    for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        m = fmaxf(m, fabsf(x[i]));
+    for (int64_t j = (n4 << 2) + tid; j < n; j += stride) m = fmaxf(m, fabsf(x[j]));
     block_max_to(m, amax);
 }
 
-// codes for n floats with the scale derived from *amax; thread t handles 16
-// consecutive elements per iteration (four v4f loads, one 16-byte store).
+// Codes for n floats with the scale derived from *amax.  Each thread takes
+// QUANT_U groups of 16 consecutive elements per iteration (4 x QUANT_U
+// independent 16-byte loads in flight), one 16-byte code store per group.
+constexpr int QUANT_U = 2;
+__device__ __forceinline__ uint4 quant16(const v4f* src, float s) {
+    v4f v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(&src[j]);
+    uint4 o;
+    o.x = e4m3x4_sat(__fdiv_rn(v[0].x, s), __fdiv_rn(v[0].y, s), __fdiv_rn(v[0].z, s), __fdiv_rn(v[0].w, s));
+    o.y = e4m3x4_sat(__fdiv_rn(v[1].x, s), __fdiv_rn(v[1].y, s), __fdiv_rn(v[1].z, s), __fdiv_rn(v[1].w, s));
+    o.z = e4m3x4_sat(__fdiv_rn(v[2].x, s), __fdiv_rn(v[2].y, s), __fdiv_rn(v[2].z, s), __fdiv_rn(v[2].w, s));
+    o.w = e4m3x4_sat(__fdiv_rn(v[3].x, s), __fdiv_rn(v[3].y, s), __fdiv_rn(v[3].z, s), __fdiv_rn(v[3].w, s));
+    return o;
+}
+
 __global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restrict__ x, int64_t n,
                                                             const float* __restrict__ amax, uint8_t* __restrict__ q,
                                                             float* scale_out) {
@@ -61,22 +86,19 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restr
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
     const int64_t n16 = n >> 4;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const v4f* x4 = reinterpret_cast<const v4f*>(x);
     uint4* q16 = reinterpret_cast<uint4*>(q);
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
-        v4f v0 = __builtin_nontemporal_load(&x4[4 * i + 0]);
-        v4f v1 = __builtin_nontemporal_load(&x4[4 * i + 1]);
-        v4f v2 = __builtin_nontemporal_load(&x4[4 * i + 2]);
-        v4f v3 = __builtin_nontemporal_load(&x4[4 * i + 3]);
-        uint4 o;
-        o.x = e4m3x4_sat(__fdiv_rn(v0.x, s), __fdiv_rn(v0.y, s), __fdiv_rn(v0.z, s), __fdiv_rn(v0.w, s));
-        o.y = e4m3x4_sat(__fdiv_rn(v1.x, s), __fdiv_rn(v1.y, s), __fdiv_rn(v1.z, s), __fdiv_rn(v1.w, s));
-        o.z = e4m3x4_sat(__fdiv_rn(v2.x, s), __fdiv_rn(v2.y, s), __fdiv_rn(v2.z, s), __fdiv_rn(v2.w, s));
-        o.w = e4m3x4_sat(__fdiv_rn(v3.x, s), __fdiv_rn(v3.y, s), __fdiv_rn(v3.z, s), __fdiv_rn(v3.w, s));
-        q16[i] = o;
+    int64_t i = tid;
+    for (; i + (QUANT_U - 1) * stride < n16; i += QUANT_U * stride) {
+        uint4 o[QUANT_U];
+#pragma unroll
+        for (int u = 0; u < QUANT_U; ++u) o[u] = quant16(x4 + 4 * (i + u * stride), s);
+#pragma unroll
+        for (int u = 0; u < QUANT_U; ++u) q16[i + u * stride] = o[u];
     }
-    for (int64_t i = (n16 << 4) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        q[i] = e4m3_sat(__fdiv_rn(x[i], s));
+    for (; i < n16; i += stride) q16[i] = quant16(x4 + 4 * i, s);
+    for (int64_t j = (n16 << 4) + tid; j < n; j += stride) q[j] = e4m3_sat(__fdiv_rn(x[j], s));
 }
 
 // 32x32 tiles: one wave per tile.  Lane l covers row l/2 of the tile, columns
@@ -199,9 +221,11 @@ int stream_blocks(int64_t work_items, int per_block) {
 
 hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, hipStream_t s) {
     hipLaunchKernelGGL(fill_f32, dim3(1), dim3(64), 0, s, amax, 1, 0.0f);
-    if (n > 0) hipLaunchKernelGGL(amax_kernel, dim3(stream_blocks(n / 4 + 1, kThreads)), dim3(kThreads), 0, s, x, n, amax);
-    hipLaunchKernelGGL(quantize_kernel, dim3(stream_blocks(n / 16 + 1, kThreads)), dim3(kThreads), 0, s, x, n,
-                       (const float*)amax, q, scale);
+    if (n > 0)
+        hipLaunchKernelGGL(amax_kernel, dim3(stream_blocks(n / (4 * AMAX_U) + 1, kThreads)), dim3(kThreads), 0, s, x, n,
+                           amax);
+    hipLaunchKernelGGL(quantize_kernel, dim3(stream_blocks(n / (16 * QUANT_U) + 1, kThreads)), dim3(kThreads), 0, s, x,
+                       n, (const float*)amax, q, scale);
     return hipGetLastError();
 }
 

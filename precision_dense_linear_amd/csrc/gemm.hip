@@ -24,12 +24,23 @@ namespace fp8k {
 
 namespace {
 
-// Operand fragments of one 64-byte K slice for a wave: TM A blocks, TN B blocks.
+// Operand fragments of one 64-byte K slice for a wave: per A block the two
+// 16-byte halves of each lane's 32 bytes, per B block the four 8-byte
+// transposed reads.
 template <int TM, int TN>
 struct Frags {
-    v8i a[TM];
-    v8i b[TN];
+    v4i a[TM][2];
+    v2i b[TN][4];
 };
+
+// Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 template <int BM, int BN, int WM, int WN, int KS, int NBUF, int GROUP_M, bool BF16, bool EXACT>
 __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
@@ -50,7 +61,8 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     const int64_t K = p.K, N = p.N;
     const int nsteps = (int)((K + KS * BKP - 1) / (KS * BKP));
     lds_u8* lds = (lds_u8*)smem;
-    const PipeLoader<BM, BN, WM, WN, KS, NBUF> loader(t, N, K, wave, lane, (uint32_t)(uintptr_t)lds);
+    using Loader = PipeLoader<BM, BN, WM, WN, KS, NBUF>;
+    const Loader loader(t, N, K, wave, lane, (uint32_t)(uintptr_t)lds);
 
     v16f acc[TM][TN];
 #pragma unroll
@@ -60,113 +72,143 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Per-lane LDS byte offsets of this wave's operands inside a stage.
-    int a_off[TM];
+    // Per-lane LDS byte offsets of this wave's operands in stage buffer 0;
+    // buffer b adds the constant b * A_STAGE (A) or b * B_STAGE (B).
+    int a_off[TM][2];
     int b_off[TN][4];
+    // the second chunk of the pair: (2h+1) ^ f = (2h ^ f) ^ 1, i.e. +-16 bytes
+    const int a_pair = (((lane & 31) >> 2) & 1) ? -16 : 16;
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
         const int row = wm * C::WTM + mi * 32 + (lane & 31);
-        a_off[mi] = ks * BM * BKP + row * BKP + swz_a64(row, (lane >> 5) * 2) * 16;
+        a_off[mi][0] = ks * BM * BKP + row * BKP + swz_a64(row, (lane >> 5) * 2) * 16;
+        a_off[mi][1] = a_off[mi][0] + a_pair;
     }
-    // the second chunk of the pair: (2h+1) ^ f = (2h ^ f) ^ 1, i.e. +-16 bytes
-    const int a_pair = (((lane & 31) >> 2) & 1) ? -16 : 16;
 #pragma unroll
     for (int ni = 0; ni < TN; ++ni) {
         const int col = wn * C::WTN + ni * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 #pragma unroll
         for (int tq = 0; tq < 4; ++tq) {
             const int kr = (lane >> 5) * 32 + ((lane & 15) >> 1) + 8 * tq;
-            b_off[ni][tq] = C::A_STAGE + ks * BKP * BN + kr * BN + swz_b<BN>(kr, col >> 4) * 16 + (col & 15);
+            b_off[ni][tq] = NBUF * C::A_STAGE + ks * BKP * BN + kr * BN + swz_b<BN>(kr, col >> 4) * 16 + (col & 15);
         }
     }
 
-    auto read_frags = [&](int st, Frags<TM, TN>& f) {
-        const lds_u8* stage = lds + (st % NBUF) * C::STAGE;
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi) {
-            const v4i lo = lds_read16(stage + a_off[mi]);
-            const v4i hi = lds_read16(stage + a_off[mi] + a_pair);
-            f.a[mi] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int ni = 0; ni < TN; ++ni) {
-            v2i q[4];
-#pragma unroll
-            for (int tq = 0; tq < 4; ++tq) q[tq] = lds_read_tr8(stage + b_off[ni][tq]);
-            f.b[ni] = (v8i){q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
-        }
-    };
-
-    // All MFMAs of one 64-byte slice.  The B fragment is the first operand, so
-    // accumulator block (mi, ni) holds C^T (see TileStore).
-    auto mma = [&](const Frags<TM, TN>& f) {
-        if constexpr (EXACT) {
-            // four K=16 BF16 MFMAs per block; chunk c of each lane's 32 bytes
-            // (K 32*(l/32) + 8c .. +7) feeds the c-th, for A and B alike.  The
-            // chunk loop is outermost, so consecutive MFMAs update different
-            // accumulators and the conversions of chunk c+1 can overlap the
-            // MFMAs of chunk c.
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                v8bf ab[TM], bb[TN];
-#pragma unroll
-                for (int mi = 0; mi < TM; ++mi) ab[mi] = e4m3x8_to_bf16(f.a[mi][2 * c], f.a[mi][2 * c + 1]);
-#pragma unroll
-                for (int ni = 0; ni < TN; ++ni) bb[ni] = e4m3x8_to_bf16(f.b[ni][2 * c], f.b[ni][2 * c + 1]);
-#pragma unroll
-                for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < TN; ++ni) acc[mi][ni] = mfma_32x32x16_bf16(bb[ni], ab[mi], acc[mi][ni]);
-            }
+    // The slice's LDS reads in a fixed order: q < 2*TM reads half q%2 of A
+    // block q/2, the rest read quarter (q-2TM)%4 of B block (q-2TM)/4.
+    constexpr int RD = 2 * TM + 4 * TN;
+    auto read_one = [&](auto q_c, auto b_c, Frags<TM, TN>& f) {
+        constexpr int q = decltype(q_c)::value, b = decltype(b_c)::value;
+        if constexpr (q < 2 * TM) {
+            f.a[q / 2][q % 2] = lds_read16(lds + b * C::A_STAGE + a_off[q / 2][q % 2]);
         } else {
+            constexpr int qb = q - 2 * TM;
+            f.b[qb / 4][qb % 4] = lds_read_tr8(lds + b * C::B_STAGE + b_off[qb / 4][qb % 4]);
+        }
+    };
+    auto a_op = [](const Frags<TM, TN>& f, int mi) {
+        const v4i lo = f.a[mi][0], hi = f.a[mi][1];
+        return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto b_op = [](const Frags<TM, TN>& f, int ni) {
+        return (v8i){f.b[ni][0][0], f.b[ni][0][1], f.b[ni][1][0], f.b[ni][1][1],
+                     f.b[ni][2][0], f.b[ni][2][1], f.b[ni][3][0], f.b[ni][3][1]};
+    };
+
+    // The slice's matrix instructions in a fixed order.  Fast: one K=64 FP8
+    // MFMA per block, index (mi, ni).  Exact: four K=16 BF16 MFMAs per block;
+    // chunk c (K 32*(l/32) + 8c .. +7 of each lane's bytes, for A and B
+    // alike) feeds MFMAs c*TM*TN .. +TM*TN-1, chunk-outermost so consecutive
+    // MFMAs update different accumulators.  The B fragment is the first
+    // operand, so accumulator block (mi, ni) holds C^T (see TileStore).
+    constexpr int BLK = TM * TN;
+    constexpr int MF = BLK * (EXACT ? 4 : 1);
+    v8bf ab[2][TM], bb[2][TN];  // exact mode: chunk c widened to BF16 in set c & 1
+    auto convert = [&](auto c_c, const Frags<TM, TN>& f) {
+        constexpr int c = decltype(c_c)::value;
 #pragma unroll
-            for (int mi = 0; mi < TM; ++mi)
+        for (int mi = 0; mi < TM; ++mi) ab[c & 1][mi] = e4m3x8_to_bf16(f.a[mi][c / 2][(c % 2) * 2], f.a[mi][c / 2][(c % 2) * 2 + 1]);
 #pragma unroll
-                for (int ni = 0; ni < TN; ++ni) acc[mi][ni] = mfma_32x32x64_e4m3(f.b[ni], f.a[mi], acc[mi][ni]);
+        for (int ni = 0; ni < TN; ++ni) bb[c & 1][ni] = e4m3x8_to_bf16(f.b[ni][c][0], f.b[ni][c][1]);
+    };
+    auto mfma_one = [&](auto m_c, const Frags<TM, TN>& f) {
+        constexpr int m = decltype(m_c)::value;
+        if constexpr (EXACT) {
+            constexpr int c = m / BLK, mi = (m % BLK) / TN, ni = m % TN;
+            acc[mi][ni] = mfma_32x32x16_bf16(bb[c & 1][ni], ab[c & 1][mi], acc[mi][ni]);
+        } else {
+            constexpr int mi = m / TN, ni = m % TN;
+            acc[mi][ni] = mfma_32x32x64_e4m3(b_op(f, ni), a_op(f, mi), acc[mi][ni]);
         }
     };
 
-    // Pipeline: stage s lives in LDS buffer s % NBUF; D = NBUF-1 stages are in
-    // flight.  Iteration s (fragments of slice s already requested):
-    //   wait until stage s+1 has landed (the D-2 newer stages may still be in
-    //   flight), barrier -- stage s+1 is visible to all waves, and every wave
-    //   has finished its MFMAs of slice s-1, hence its reads of buffer
-    //   (s-1) % NBUF = (s+D) % NBUF;
-    //   issue stage s+D into that buffer;
-    //   read the slice s+1 fragments while the slice s MFMAs run.
+    // Pipeline: stage s lives in LDS buffer s % NBUF; all NBUF buffers are in
+    // flight.  Slice s, whose fragments are already requested:
+    //   wait until stage s+1 has landed (the NBUF-2 newer stages may still be
+    //   in flight) and this wave's LDS reads are complete; barrier -- stage s+1
+    //   is visible to all waves, and no wave still reads buffer s % NBUF (its
+    //   fragments are in registers), so stage s+NBUF may refill it;
+    //   then LPS regions, each: a share of the slice s+1 LDS reads, a share of
+    //   the slice s MFMAs, and one of the wave's LPS loads of stage s+NBUF.
+    // Spreading the loads between the MFMAs keeps the four waves from
+    // queueing a whole stage of loads at once behind the barrier, which
+    // stalls each wave's MFMA issue until the address unit has accepted them.
     // Loads past the end of K are empty (they read zero), so the body is
-    // branch-free and the in-flight load count is the same every iteration.
-    constexpr int D = NBUF - 1;
-    constexpr int MF = TM * TN * (EXACT ? 4 : 1);  // MFMA instructions per slice
-    constexpr int RD = 2 * TM + 4 * TN;             // LDS reads per slice
+    // branch-free and the in-flight load count is the same every stage.  The
+    // loop is unrolled over whole buffer cycles (and fragment register pairs),
+    // so every LDS address is a base register plus an immediate; the slice
+    // count is rounded up to whole loop bodies, the extra slices multiplying
+    // zeros (an accumulator that starts at +0 stays exact under +0 terms).
+    constexpr int G = C::LPS;                     // regions per slice
+    constexpr int U = (NBUF % 2) ? 2 * NBUF : NBUF;  // slices per unrolled body
     Frags<TM, TN> f0, f1;
 #pragma unroll
-    for (int st = 0; st < D; ++st) loader.issue(st);
-    wait_vmcnt<(D - 1) * C::LPS>();
+    for (int st = 0; st < NBUF; ++st) loader.issue(st);
+    wait_vmcnt_lds<(NBUF - 1) * C::LPS>();
     __syncthreads();
-    read_frags(0, f0);
+    static_for<0, RD>([&](auto q_c) { read_one(q_c, std::integral_constant<int, 0>{}, f0); });
 
-    auto iteration = [&](int s, Frags<TM, TN>& cur, Frags<TM, TN>& next) {
-        wait_vmcnt<(D - 2) * C::LPS>();
-        __syncthreads();
-        loader.issue(s + D);
-        read_frags(s + 1, next);
-        mma(cur);
-        // interleave: the next fragment's LDS reads spread over the MFMAs
-        constexpr int RPM = (RD + MF - 1) / MF;
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
+        static_for<0, U>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int bn = (i + 1) % NBUF;  // buffer of slice s+1 (s0 is a multiple of NBUF)
+            const Frags<TM, TN>& cur = (i & 1) ? f1 : f0;
+            Frags<TM, TN>& next = (i & 1) ? f0 : f1;
+            wait_vmcnt_lds<(NBUF - 2) * C::LPS>();
+            __syncthreads();
+            const typename Loader::Stage stage = loader.prepare(s0 + i + NBUF);
+            static_for<0, G>([&](auto r_c) {
+                constexpr int r = decltype(r_c)::value;
+                constexpr int q0 = RD * r / G, q1 = RD * (r + 1) / G;
+                constexpr int m0 = MF * r / G, m1 = MF * (r + 1) / G;
+                if constexpr (EXACT) {
+                    // widen chunk 0 ahead of its MFMAs; chunk c >= 1 one region
+                    // early (in the region holding MFMA c*BLK - 1), so the
+                    // conversions overlap the previous chunk's MFMAs
+                    if constexpr (r == 0) convert(std::integral_constant<int, 0>{}, cur);
+                    static_for<1, 4>([&](auto c_c) {
+                        constexpr int c = decltype(c_c)::value;
+                        if constexpr (c * BLK - 1 >= m0 && c * BLK - 1 < m1) convert(c_c, cur);
+                    });
+                }
+                static_for<q0, q1>([&](auto q_c) { read_one(q_c, std::integral_constant<int, bn>{}, next); });
+                static_for<m0, m1>([&](auto m_c) { mfma_one(m_c, cur); });
+                // interleave the region's LDS reads with its MFMAs
+                constexpr int nq = q1 - q0, nm = m1 - m0;
+                if constexpr (nm > 0 && nq > 0) {
+                    constexpr int RPM = (nq + nm - 1) / nm;
 #pragma unroll
-        for (int i = 0; i < (RD + RPM - 1) / RPM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    int s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-        iteration(s, f0, f1);
-        iteration(s + 1, f1, f0);
+                    for (int g = 0; g < (nq + RPM - 1) / RPM; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS read
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                loader.issue_one(stage, r);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
     }
-    if (s < nsteps) iteration(s, f0, f1);
 
     // Drain: the empty tail loads must land before the LDS is reused.
     wait_vmcnt<0>();

@@ -197,14 +197,16 @@ struct StageLoader {
 };
 
 // ---------------------------------------------------------------------------
-// Deep pipeline (per-tensor and grouped GEMM): stages of 64 bytes of K per
-// wave group, NBUF stage buffers in LDS, NBUF-1 stages in flight.
+// Deep pipeline (per-tensor and grouped GEMM).  A stage holds 64 bytes of K
+// per wave group; NBUF stage buffers live in LDS, the NBUF A parts first and
+// then the NBUF B parts, and a buffer is refilled as soon as its fragments
+// are in registers, so NBUF stages are in flight.
 //  * A stage: KS sub-tiles of [BM rows][64 bytes]; chunk c of row r sits at
 //    position c ^ ((r >> 2) & 3), so the 16 rows of one ds_read_b128 phase
-//    (four rows per 256-byte bank window) hit 16 distinct chunks.
+//    (four rows per 256-byte bank window) hit 16 distinct 16-byte bank groups.
 //  * B stage: KS sub-tiles of [64 K-rows][BN bytes], swizzled as swz_b.
 // ---------------------------------------------------------------------------
-constexpr int BKP = 64;  // bytes of K per wave group per pipelined stage
+constexpr int BKP = 64;  // bytes of K per wave group per stage
 
 __device__ __forceinline__ int swz_a64(int row, int c) { return c ^ ((row >> 2) & 3); }
 
@@ -225,7 +227,7 @@ struct PipeCfg {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "stage loads must split evenly over waves");
     static_assert(BN >= 64 && BN <= 256 && (BN & (BN - 1)) == 0, "BN must be 64, 128 or 256");
-    static_assert(NBUF >= 3 && (NBUF - 3) * LPS <= 63, "in-flight loads must fit the vmcnt counter");
+    static_assert(NBUF >= 2 && (NBUF - 1) * LPS <= 63, "in-flight loads must fit the vmcnt counter");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -248,6 +250,15 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N <= 63, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0): also every LDS read this wave has issued is
+// complete (its data is in registers), so after a following barrier no wave
+// still reads the buffers whose fragments are already loaded.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
 template <int BM, int BN, int WM, int WN, int KS, int NBUF>
@@ -290,19 +301,38 @@ struct PipeLoader {
         }
     }
 
-    // Stage `st` (K bytes [st*KS*64, +KS*64)) into LDS buffer st % NBUF.  Past
-    // the end of K the resources are empty, so every load reads zero.
-    __device__ __forceinline__ void issue(int st) const {
+    // Stage `st` (K bytes [st*KS*64, +KS*64)) into LDS buffer st % NBUF: its
+    // A part at offset (st % NBUF) * A_STAGE, its B part after all NBUF A
+    // parts.  Past the end of K the resources are empty, so every load reads
+    // zero.  prepare() builds the stage's resources (scalar work); issue_one(i)
+    // enqueues the wave's i-th of its LPS loads, so a kernel can spread them
+    // between its matrix instructions.
+    struct Stage {
+        __amdgpu_buffer_rsrc_t ra, rb;
+        int64_t krem;
+        uint32_t dst_a, dst_b;
+    };
+    __device__ __forceinline__ Stage prepare(int st) const {
+        Stage g;
         const int64_t k0 = (int64_t)st * (KS * BKP);
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + k0, clamp_records(a_bytes - k0));
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + k0 * N, clamp_records(b_bytes - k0 * N));
-        const int64_t krem = K - k0;
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_wave + (uint32_t)(st % NBUF) * C::STAGE);
+        g.ra = make_rsrc(a_base + k0, clamp_records(a_bytes - k0));
+        g.rb = make_rsrc(b_base + k0 * N, clamp_records(b_bytes - k0 * N));
+        g.krem = K - k0;
+        const uint32_t b = (uint32_t)(st % NBUF);
+        g.dst_a = __builtin_amdgcn_readfirstlane(lds_wave + b * C::A_STAGE);
+        g.dst_b = __builtin_amdgcn_readfirstlane(lds_wave + NBUF * C::A_STAGE + b * C::B_STAGE);
+        return g;
+    }
+    __device__ __forceinline__ void issue_one(const Stage& g, int i) const {
+        if (i < C::NA)
+            dma16(g.ra, g.dst_a + i * C::NW * 1024, (int64_t)a_kk[i] < g.krem ? a_off[i] : OOB);
+        else
+            dma16(g.rb, g.dst_b + (i - C::NA) * C::NW * 1024, b_off[i - C::NA]);
+    }
+    __device__ __forceinline__ void issue(int st) const {
+        const Stage g = prepare(st);
 #pragma unroll
-        for (int i = 0; i < C::NA; ++i)
-            dma16(ra, dst + i * C::NW * 1024, (int64_t)a_kk[i] < krem ? a_off[i] : OOB);
-#pragma unroll
-        for (int i = 0; i < C::NB; ++i) dma16(rb, dst + C::A_STAGE + i * C::NW * 1024, b_off[i]);
+        for (int i = 0; i < C::LPS; ++i) issue_one(g, i);
     }
 };
 

@@ -42,9 +42,9 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int KS, int NBUF, int GROUP_M, bool BF16, bool EXACT>
+template <int BM, int BN, int WM, int WN, int KS, int GROUP_M, bool BF16, bool EXACT>
 __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
-    using C = PipeCfg<BM, BN, WM, WN, KS, NBUF>;
+    using C = PipeCfg<BM, BN, WM, WN, KS>;
     constexpr int TM = C::TM, TN = C::TN;
     constexpr int EPI = (KS > 1 ? C::RED : 0) + WM * WN * TileStore<BF16, TM, TN>::LDS_BYTES;
     static_assert(EPI <= 160 * 1024, "epilogue LDS budget");
@@ -59,9 +59,10 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     const int wm = (wave % (WM * WN)) / WN;
     const int wn = wave % WN;
     const int64_t K = p.K, N = p.N;
-    const int nsteps = (int)((K + KS * BKP - 1) / (KS * BKP));
+    // slices per wave group: whole A stages of KS * 128 bytes of K
+    const int nsteps = 2 * (int)((K + KS * BKA - 1) / (KS * BKA));
     lds_u8* lds = (lds_u8*)smem;
-    using Loader = PipeLoader<BM, BN, WM, WN, KS, NBUF>;
+    using Loader = PipeLoader<BM, BN, WM, WN, KS>;
     const Loader loader(t, N, K, wave, lane, (uint32_t)(uintptr_t)lds);
 
     v16f acc[TM][TN];
@@ -72,17 +73,20 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Per-lane LDS byte offsets of this wave's operands in stage buffer 0;
-    // buffer b adds the constant b * A_STAGE (A) or b * B_STAGE (B).
-    int a_off[TM][2];
+    // Per-lane LDS byte offsets of this wave's operands: A in A stage 0 for
+    // both slices u of a stage and both 16-byte halves h of a lane's 32 bytes
+    // (lane l wants chunks 4u + 2(l/32) + h of its row, each at its XOR
+    // position), B in B stage 0 (a B stage adds the constant j * B_STAGE).
+    int a_off[2][TM][2];
     int b_off[TN][4];
-    // the second chunk of the pair: (2h+1) ^ f = (2h ^ f) ^ 1, i.e. +-16 bytes
-    const int a_pair = (((lane & 31) >> 2) & 1) ? -16 : 16;
 #pragma unroll
     for (int mi = 0; mi < TM; ++mi) {
         const int row = wm * C::WTM + mi * 32 + (lane & 31);
-        a_off[mi][0] = ks * BM * BKP + row * BKP + swz_a64(row, (lane >> 5) * 2) * 16;
-        a_off[mi][1] = a_off[mi][0] + a_pair;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                a_off[u][mi][h] = ks * BM * BKA + row * BKA + swz_a128(row, 4 * u + (lane >> 5) * 2 + h) * 16;
     }
 #pragma unroll
     for (int ni = 0; ni < TN; ++ni) {
@@ -90,20 +94,22 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int tq = 0; tq < 4; ++tq) {
             const int kr = (lane >> 5) * 32 + ((lane & 15) >> 1) + 8 * tq;
-            b_off[ni][tq] = NBUF * C::A_STAGE + ks * BKP * BN + kr * BN + swz_b<BN>(kr, col >> 4) * 16 + (col & 15);
+            b_off[ni][tq] = C::B_BASE + ks * BKP * BN + kr * BN + swz_b<BN>(kr, col >> 4) * 16 + (col & 15);
         }
     }
 
-    // The slice's LDS reads in a fixed order: q < 2*TM reads half q%2 of A
+    // A slice's LDS reads in a fixed order: q < 2*TM reads half q%2 of A
     // block q/2, the rest read quarter (q-2TM)%4 of B block (q-2TM)/4.
+    // `abuf` is the LDS address of the slice's A stage; U (slice within the
+    // A stage) and BB (B stage buffer) are compile-time.
     constexpr int RD = 2 * TM + 4 * TN;
-    auto read_one = [&](auto q_c, auto b_c, Frags<TM, TN>& f) {
-        constexpr int q = decltype(q_c)::value, b = decltype(b_c)::value;
+    auto read_one = [&](auto q_c, auto u_c, auto bb_c, const lds_u8* abuf, Frags<TM, TN>& f) {
+        constexpr int q = decltype(q_c)::value, u = decltype(u_c)::value, bb = decltype(bb_c)::value;
         if constexpr (q < 2 * TM) {
-            f.a[q / 2][q % 2] = lds_read16(lds + b * C::A_STAGE + a_off[q / 2][q % 2]);
+            f.a[q / 2][q % 2] = lds_read16(abuf + a_off[u][q / 2][q % 2]);
         } else {
             constexpr int qb = q - 2 * TM;
-            f.b[qb / 4][qb % 4] = lds_read_tr8(lds + b * C::B_STAGE + b_off[qb / 4][qb % 4]);
+            f.b[qb / 4][qb % 4] = lds_read_tr8(lds + bb * C::B_STAGE + b_off[qb / 4][qb % 4]);
         }
     };
     auto a_op = [](const Frags<TM, TN>& f, int mi) {
@@ -142,41 +148,47 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
         }
     };
 
-    // Pipeline: stage s lives in LDS buffer s % NBUF; all NBUF buffers are in
-    // flight.  Slice s, whose fragments are already requested:
-    //   wait until stage s+1 has landed (the NBUF-2 newer stages may still be
-    //   in flight) and this wave's LDS reads are complete; barrier -- stage s+1
-    //   is visible to all waves, and no wave still reads buffer s % NBUF (its
-    //   fragments are in registers), so stage s+NBUF may refill it;
+    // Pipeline (load schedule in PipeLoader).  Slice s, whose fragments are
+    // already in registers or requested:
+    //   wait until the loads of slice s-3 and earlier have landed (the later
+    //   two slices' loads may still be in flight) and this wave's LDS reads
+    //   are complete; barrier -- the stages that slice s+1 reads are visible to
+    //   all waves, and no wave still reads the buffers slice s refills;
     //   then LPS regions, each: a share of the slice s+1 LDS reads, a share of
-    //   the slice s MFMAs, and one of the wave's LPS loads of stage s+NBUF.
+    //   the slice s MFMAs, and one of the slice's LPS loads.
     // Spreading the loads between the MFMAs keeps the four waves from
     // queueing a whole stage of loads at once behind the barrier, which
     // stalls each wave's MFMA issue until the address unit has accepted them.
     // Loads past the end of K are empty (they read zero), so the body is
-    // branch-free and the in-flight load count is the same every stage.  The
-    // loop is unrolled over whole buffer cycles (and fragment register pairs),
-    // so every LDS address is a base register plus an immediate; the slice
-    // count is rounded up to whole loop bodies, the extra slices multiplying
-    // zeros (an accumulator that starts at +0 stays exact under +0 terms).
-    constexpr int G = C::LPS;                     // regions per slice
-    constexpr int U = (NBUF % 2) ? 2 * NBUF : NBUF;  // slices per unrolled body
+    // branch-free and the in-flight load count is the same every slice.  The
+    // loop is unrolled over the four B buffers (and fragment register pairs);
+    // the slice count is a whole number of A stages, and rounded up to whole
+    // loop bodies, the extra slices multiplying zeros (an accumulator that
+    // starts at +0 stays exact under +0 terms).
+    constexpr int G = C::LPS;  // regions per slice
+    constexpr int U = NBUF_B;  // slices per unrolled body
+    static_assert(U % 2 == 0, "fragment register pairs and A-stage halves alternate");
     Frags<TM, TN> f0, f1;
+    loader.issue_a_half(-5);
 #pragma unroll
-    for (int st = 0; st < NBUF; ++st) loader.issue(st);
-    wait_vmcnt_lds<(NBUF - 1) * C::LPS>();
+    for (int s = -4; s < 0; ++s) loader.issue_slice(s);
+    wait_vmcnt_lds<3 * C::LPS>();
     __syncthreads();
-    static_for<0, RD>([&](auto q_c) { read_one(q_c, std::integral_constant<int, 0>{}, f0); });
+    static_for<0, RD>([&](auto q_c) {
+        read_one(q_c, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, lds, f0);
+    });
 
     for (int s0 = 0; s0 < nsteps; s0 += U) {
         static_for<0, U>([&](auto i_c) {
             constexpr int i = decltype(i_c)::value;
-            constexpr int bn = (i + 1) % NBUF;  // buffer of slice s+1 (s0 is a multiple of NBUF)
+            const int s = s0 + i;
             const Frags<TM, TN>& cur = (i & 1) ? f1 : f0;
             Frags<TM, TN>& next = (i & 1) ? f0 : f1;
-            wait_vmcnt_lds<(NBUF - 2) * C::LPS>();
+            wait_vmcnt_lds<2 * C::LPS>();
             __syncthreads();
-            const typename Loader::Stage stage = loader.prepare(s0 + i + NBUF);
+            const typename Loader::Stage stage = loader.prepare(s);
+            // slice s+1: A stage (s+1)/2, slice (i+1)&1 of it; B buffer (i+1)%4
+            const lds_u8* abuf = lds + (((s + 1) >> 1) % NBUF_A) * C::A_STAGE;
             static_for<0, G>([&](auto r_c) {
                 constexpr int r = decltype(r_c)::value;
                 constexpr int q0 = RD * r / G, q1 = RD * (r + 1) / G;
@@ -191,7 +203,10 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
                         if constexpr (c * BLK - 1 >= m0 && c * BLK - 1 < m1) convert(c_c, cur);
                     });
                 }
-                static_for<q0, q1>([&](auto q_c) { read_one(q_c, std::integral_constant<int, bn>{}, next); });
+                static_for<q0, q1>([&](auto q_c) {
+                    read_one(q_c, std::integral_constant<int, (i + 1) & 1>{}, std::integral_constant<int, (i + 1) % U>{},
+                             abuf, next);
+                });
                 static_for<m0, m1>([&](auto m_c) { mfma_one(m_c, cur); });
                 // interleave the region's LDS reads with its MFMAs
                 constexpr int nq = q1 - q0, nm = m1 - m0;
@@ -204,7 +219,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                loader.issue_one(stage, r);
+                loader.issue_one(stage, r, (i + 1) & 1);
                 __builtin_amdgcn_sched_barrier(0);
             });
         });
@@ -252,7 +267,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch);
 }
 
-template <int BM, int BN, int WM, int WN, int KS, int NBUF, int GROUP_M>
+template <int BM, int BN, int WM, int WN, int KS, int GROUP_M>
 hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
     GemmArgs a;
     a.A = g.A;
@@ -274,11 +289,11 @@ hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
     constexpr int NT = 64 * WM * WN * KS;
     const dim3 grid((unsigned)blocks), block(NT);
     if (g.fast_acc) {
-        if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NBUF, GROUP_M, true, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NBUF, GROUP_M, false, false>), grid, block, 0, s, a);
+        if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, true, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, false, false>), grid, block, 0, s, a);
     } else {
-        if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NBUF, GROUP_M, true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NBUF, GROUP_M, false, true>), grid, block, 0, s, a);
+        if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, false, true>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -292,9 +307,9 @@ hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
 //  * larger M: 256 x 256 tiles, 4 waves of 128 x 128 -- MFMA bound.
 hipError_t launch_gemm(const GemmProblem& g, hipStream_t s) {
     const int64_t rows_per_problem = g.experts ? (g.M + g.experts - 1) / g.experts : g.M;
-    if (rows_per_problem <= 64) return launch_cfg<32, 64, 1, 2, 2, 4, 8>(g, s);
-    if (rows_per_problem <= 1024) return launch_cfg<128, 128, 2, 2, 1, 4, 8>(g, s);
-    return launch_cfg<256, 256, 2, 2, 1, 4, 8>(g, s);
+    if (rows_per_problem <= 64) return launch_cfg<32, 64, 1, 2, 2, 8>(g, s);
+    if (rows_per_problem <= 1024) return launch_cfg<128, 128, 2, 2, 1, 8>(g, s);
+    return launch_cfg<256, 256, 2, 2, 1, 8>(g, s);
 }
 
 }  // namespace fp8k

@@ -197,37 +197,43 @@ struct StageLoader {
 };
 
 // ---------------------------------------------------------------------------
-// Deep pipeline (per-tensor and grouped GEMM).  A stage holds 64 bytes of K
-// per wave group; NBUF stage buffers live in LDS, the NBUF A parts first and
-// then the NBUF B parts, and a buffer is refilled as soon as its fragments
-// are in registers, so NBUF stages are in flight.
-//  * A stage: KS sub-tiles of [BM rows][64 bytes]; chunk c of row r sits at
-//    position c ^ ((r >> 2) & 3), so the 16 rows of one ds_read_b128 phase
-//    (four rows per 256-byte bank window) hit 16 distinct 16-byte bank groups.
-//  * B stage: KS sub-tiles of [64 K-rows][BN bytes], swizzled as swz_b.
+// Deep pipeline (per-tensor and grouped GEMM).  The MFMA loop walks slices of
+// 64 bytes of K per wave group.  A is staged 128 bytes of K (two slices) at a
+// time, so every A row of a stage is one whole 128-byte line and each A load
+// is a full-line L2 request; B is staged one slice (64 K-rows of BN bytes,
+// two whole lines per row for BN = 256) at a time.  LDS holds NBUF_A = 3 A
+// stages and then NBUF_B = 4 B stages.
+//  * A stage: KS sub-tiles of [BM rows][128 bytes]; chunk c of row r sits at
+//    position c ^ ((r >> 1) & 7), so the 16 rows of one ds_read_b128 phase
+//    (two rows per 256-byte bank window) hit 16 distinct 16-byte bank groups.
+//    Wave group ks takes bytes [128 ks, 128 ks + 128) of each A stage.
+//  * B stage j: KS sub-tiles of [64 K-rows][BN bytes], swizzled as swz_b;
+//    sub-tile ks holds the K-rows that wave group ks multiplies in slice j.
 // ---------------------------------------------------------------------------
-constexpr int BKP = 64;  // bytes of K per wave group per stage
+constexpr int BKP = 64;   // bytes of K per slice (one K step of the MFMA loop)
+constexpr int BKA = 128;  // bytes of K per wave group per A stage
+constexpr int NBUF_A = 3, NBUF_B = 4;
 
-__device__ __forceinline__ int swz_a64(int row, int c) { return c ^ ((row >> 2) & 3); }
+__device__ __forceinline__ int swz_a128(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-template <int BM, int BN, int WM, int WN, int KS, int NBUF>
+template <int BM, int BN, int WM, int WN, int KS>
 struct PipeCfg {
     static constexpr int NW = WM * WN * KS;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
-    static constexpr int A_STAGE = KS * BM * BKP;
+    static constexpr int A_STAGE = KS * BM * BKA;
     static constexpr int B_STAGE = KS * BKP * BN;
-    static constexpr int STAGE = A_STAGE + B_STAGE;
-    static constexpr int A_INSTR = A_STAGE / 1024;
-    static constexpr int B_INSTR = B_STAGE / 1024;
-    static constexpr int NA = A_INSTR / NW, NB = B_INSTR / NW;
-    static constexpr int LPS = NA + NB;  // global->LDS loads per wave per stage
+    static constexpr int B_BASE = NBUF_A * A_STAGE;  // LDS offset of the B stages
+    static constexpr int NA = A_STAGE / 1024 / NW;   // loads per wave per A stage
+    static constexpr int NB = B_STAGE / 1024 / NW;   // loads per wave per B stage
+    static constexpr int LPS = NB + NA / 2;          // loads per wave per slice
     static constexpr int RED = (KS > 1) ? (KS - 1) * BM * BN * 4 : 0;
-    static constexpr int LDS = NBUF * STAGE;
+    static constexpr int LDS = B_BASE + NBUF_B * B_STAGE;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "stage loads must split evenly over waves");
+    static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "stage loads must split evenly over waves");
+    static_assert(NA % 2 == 0, "an A stage is issued in two halves");
     static_assert(BN >= 64 && BN <= 256 && (BN & (BN - 1)) == 0, "BN must be 64, 128 or 256");
-    static_assert(NBUF >= 2 && (NBUF - 1) * LPS <= 63, "in-flight loads must fit the vmcnt counter");
+    static_assert(3 * LPS <= 63, "in-flight loads must fit the vmcnt counter");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -261,14 +267,19 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-template <int BM, int BN, int WM, int WN, int KS, int NBUF>
+// Load schedule: slice s issues B stage s+4 and one half of A stage
+// (s+5)/2 (half (s+1)&1), LPS loads per wave in all.  Stage data is thus
+// issued three slices before the slice whose fragment reads need it, and a
+// buffer is refilled only after the barrier that follows the reads of its
+// last fragments.
+template <int BM, int BN, int WM, int WN, int KS>
 struct PipeLoader {
-    using C = PipeCfg<BM, BN, WM, WN, KS, NBUF>;
+    using C = PipeCfg<BM, BN, WM, WN, KS>;
     uint32_t a_off[C::NA], a_kk[C::NA], b_off[C::NB];
     const uint8_t* a_base;
     const uint8_t* b_base;
     int64_t a_bytes, b_bytes, K, N;
-    uint32_t lds_wave;  // LDS byte address of this wave's first 1 KiB slot in buffer 0
+    uint32_t lds_wave;  // LDS byte address of this wave's first 1 KiB slot
 
     __device__ __forceinline__ PipeLoader(const TileSlice& t, int64_t N_, int64_t K_, int wave, int lane,
                                           uint32_t lds_base) {
@@ -283,10 +294,10 @@ struct PipeLoader {
 #pragma unroll
         for (int i = 0; i < C::NA; ++i) {
             const int slot = (i * C::NW + wave) * 64 + lane;
-            const int sub = slot / (BM * 4);
-            const int s2 = slot % (BM * 4);
-            const int row = s2 >> 2;
-            const int kk = sub * BKP + swz_a64(row, s2 & 3) * 16;
+            const int sub = slot / (BM * 8);
+            const int s2 = slot % (BM * 8);
+            const int row = s2 >> 3;
+            const int kk = sub * BKA + swz_a128(row, s2 & 7) * 16;
             a_kk[i] = kk;
             a_off[i] = row < rows_here ? (uint32_t)(row * K + kk) : OOB;
         }
@@ -297,42 +308,53 @@ struct PipeLoader {
             const int s2 = slot % (BKP * BN / 16);
             const int r = s2 / (BN / 16);
             const int c = swz_b<BN>(r, s2 % (BN / 16));
-            b_off[i] = (t.n0 + c * 16 < N) ? (uint32_t)((sub * BKP + r) * N + c * 16) : OOB;
+            b_off[i] = (t.n0 + c * 16 < N) ? (uint32_t)((sub * BKA + r) * N + c * 16) : OOB;
         }
     }
 
-    // Stage `st` (K bytes [st*KS*64, +KS*64)) into LDS buffer st % NBUF: its
-    // A part at offset (st % NBUF) * A_STAGE, its B part after all NBUF A
-    // parts.  Past the end of K the resources are empty, so every load reads
-    // zero.  prepare() builds the stage's resources (scalar work); issue_one(i)
-    // enqueues the wave's i-th of its LPS loads, so a kernel can spread them
-    // between its matrix instructions.
+    // The loads of slice s (see above): resources and LDS destinations.  Past
+    // the end of K the resources are empty, so every load reads zero.
     struct Stage {
         __amdgpu_buffer_rsrc_t ra, rb;
         int64_t krem;
         uint32_t dst_a, dst_b;
     };
-    __device__ __forceinline__ Stage prepare(int st) const {
+    __device__ __forceinline__ Stage prepare(int s) const {
         Stage g;
-        const int64_t k0 = (int64_t)st * (KS * BKP);
-        g.ra = make_rsrc(a_base + k0, clamp_records(a_bytes - k0));
-        g.rb = make_rsrc(b_base + k0 * N, clamp_records(b_bytes - k0 * N));
-        g.krem = K - k0;
-        const uint32_t b = (uint32_t)(st % NBUF);
-        g.dst_a = __builtin_amdgcn_readfirstlane(lds_wave + b * C::A_STAGE);
-        g.dst_b = __builtin_amdgcn_readfirstlane(lds_wave + NBUF * C::A_STAGE + b * C::B_STAGE);
+        const int jb = s + NBUF_B;     // B stage
+        const int ja = (s + 5) >> 1;   // A stage
+        const int64_t kb0 = (int64_t)(jb >> 1) * (KS * BKA) + (jb & 1) * BKP;
+        const int64_t ka0 = (int64_t)ja * (KS * BKA);
+        g.ra = make_rsrc(a_base + ka0, clamp_records(a_bytes - ka0));
+        g.rb = make_rsrc(b_base + kb0 * N, clamp_records(b_bytes - kb0 * N));
+        g.krem = K - ka0;
+        g.dst_a = __builtin_amdgcn_readfirstlane(lds_wave + (uint32_t)(ja % NBUF_A) * C::A_STAGE);
+        g.dst_b = __builtin_amdgcn_readfirstlane(lds_wave + C::B_BASE + (uint32_t)(jb % NBUF_B) * C::B_STAGE);
         return g;
     }
-    __device__ __forceinline__ void issue_one(const Stage& g, int i) const {
-        if (i < C::NA)
+    // Load r (0 <= r < LPS) of a slice whose A half is `half`: the NB B loads
+    // first, then the A stage's loads [half * NA/2, half * NA/2 + NA/2).
+    __device__ __forceinline__ void issue_one(const Stage& g, int r, int half) const {
+        if (r < C::NB) {
+            dma16(g.rb, g.dst_b + r * C::NW * 1024, b_off[r]);
+        } else {
+            const int i = half * (C::NA / 2) + (r - C::NB);
             dma16(g.ra, g.dst_a + i * C::NW * 1024, (int64_t)a_kk[i] < g.krem ? a_off[i] : OOB);
-        else
-            dma16(g.rb, g.dst_b + (i - C::NA) * C::NW * 1024, b_off[i - C::NA]);
+        }
     }
-    __device__ __forceinline__ void issue(int st) const {
-        const Stage g = prepare(st);
+    // A slice's loads all at once (the pipeline prologue).
+    __device__ __forceinline__ void issue_slice(int s) const {
+        const Stage g = prepare(s);
+        const int half = (s + 1) & 1;
 #pragma unroll
-        for (int i = 0; i < C::LPS; ++i) issue_one(g, i);
+        for (int r = 0; r < C::LPS; ++r) issue_one(g, r, half);
+    }
+    // Only the A half of slice s (the first load of the prologue).
+    __device__ __forceinline__ void issue_a_half(int s) const {
+        const Stage g = prepare(s);
+        const int half = (s + 1) & 1;
+#pragma unroll
+        for (int r = C::NB; r < C::LPS; ++r) issue_one(g, r, half);
     }
 };
 

@@ -27,13 +27,22 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file additions.  gemm_blockscaled.hip: every MFMA result goes to the
+# architectural VGPRs, where the vector FMAs that fold the block-scaled
+# partial products can read it (the default heuristics put it in the
+# accumulation registers, which VALU instructions can only copy out of).
+FILE_FLAGS = {
+    "gemm_blockscaled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC] + COMMON_FLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + COMMON_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l and "not a recognized feature" not in l)
     if r.returncode != 0:

@@ -30,15 +30,10 @@ __device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
     return bytes <= 0 ? 0u : (bytes >= (int64_t)OOB ? OOB : (uint32_t)bytes);
 }
 
-// One wave stores 64 x 16 bytes from global memory straight into LDS: lane l's
-// 16 bytes land at lds_wave_base + 16*l (buffer_load_dwordx4 ... lds).
-__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, lds_u8* lds_wave_base, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, 0, 0, 0);
-}
-
 // D = A(32x64) * B(64x32) + C with OCP E4M3 operands, FP32 accumulate
 // (v_mfma_f32_32x32x64_f8f6f4; zero scale operands select the unscaled form).
-// Lane l holds A row l%32 / B column l%32, K bytes 32*(l/32) .. +31;
+// Lane l holds A row l%32 / B column l%32, K positions 32*(l/32) .. +31 of
+// the instruction;
 // accumulator element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 __device__ __forceinline__ v16f mfma_32x32x64_e4m3(v8i a, v8i b, v16f c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);

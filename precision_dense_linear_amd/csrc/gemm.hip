@@ -1,301 +1,15 @@
-// Per-tensor scaled FP8 GEMM and its MoE grouped form, for gfx950.
-//
-//   C[m, n] = (scale_a * scale_b) * sum_k A[m, k] * B[k, n]
-//
-// E4M3 operands, FP32 accumulation, the scales applied once to the finished
-// sum, FP32 or BF16 (RNE) output ("Triton FP8 GEMM via CUTLASS naming": kernel
-// section, the paragraph after it and the parameter list).  A is M x K with K
-// contiguous and B is K x N with N contiguous, as in the kernel sketch of
-// "FP8 GEMM in JAX with Triton for Blackwell"; the grouped form runs the same
-// tile loop over expert row ranges with per-expert scales (that page's MoE
-// paragraph).
-//
-// Operand feed per 64-byte K slice (v_mfma_f32_32x32x64_f8f6f4):
-//  * A: lane l reads row l%32 of its 32-row block, K bytes 32*(l/32)..+31,
-//    as two ds_read_b128 from the swizzled A stage;
-//  * B: lane l needs column l%32 with the same 32 K bytes; four
-//    ds_read_b64_tr_b8 reads each gather 8 K-consecutive bytes of one column
-//    from the N-contiguous B stage (the 16 lanes of a group address 8 K-rows
-//    x two 8-byte column halves; lane 8h+c receives column c of half h).
-#include "gemm_common.h"
-#include "launch.h"
+// Per-tensor scaled FP8 GEMM and its MoE grouped form, for gfx950: tile
+// configuration by shape class over the tile loop of gemm_kernel.h.
+#include "gemm_kernel.h"
 
 namespace fp8k {
 
 namespace {
 
-// Operand fragments of one 64-byte K slice for a wave: per A block the two
-// 16-byte halves of each lane's 32 bytes, per B block the four 8-byte
-// transposed reads.
-template <int TM, int TN>
-struct Frags {
-    v4i a[TM][2];
-    v2i b[TN][4];
-};
-
-// Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
-template <int BM, int BN, int WM, int WN, int KS, int GROUP_M, bool BF16, bool EXACT>
-__global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
-    using C = PipeCfg<BM, BN, WM, WN, KS>;
-    constexpr int TM = C::TM, TN = C::TN;
-    constexpr int EPI = (KS > 1 ? C::RED : 0) + WM * WN * TileStore<BF16, TM, TN>::LDS_BYTES;
-    static_assert(EPI <= 160 * 1024, "epilogue LDS budget");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS > EPI ? C::LDS : EPI];
-
-    const TileSlice t = resolve_tile<BM, BN, GROUP_M>(p);
-    if (!t.valid) return;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ks = wave / (WM * WN);
-    const int wm = (wave % (WM * WN)) / WN;
-    const int wn = wave % WN;
-    const int64_t K = p.K, N = p.N;
-    // slices per wave group: whole A stages of KS * 128 bytes of K
-    const int nsteps = 2 * (int)((K + KS * BKA - 1) / (KS * BKA));
-    lds_u8* lds = (lds_u8*)smem;
-    using Loader = PipeLoader<BM, BN, WM, WN, KS>;
-    const Loader loader(t, N, K, wave, lane, (uint32_t)(uintptr_t)lds);
-
-    v16f acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // Per-lane LDS byte offsets of this wave's operands: A in A stage 0 for
-    // both slices u of a stage and both 16-byte halves h of a lane's 32 bytes
-    // (lane l wants chunks 4u + 2(l/32) + h of its row, each at its XOR
-    // position), B in B stage 0 (a B stage adds the constant j * B_STAGE).
-    int a_off[2][TM][2];
-    int b_off[TN][4];
-#pragma unroll
-    for (int mi = 0; mi < TM; ++mi) {
-        const int row = wm * C::WTM + mi * 32 + (lane & 31);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                a_off[u][mi][h] = ks * BM * BKA + row * BKA + swz_a128(row, 4 * u + (lane >> 5) * 2 + h) * 16;
-    }
-#pragma unroll
-    for (int ni = 0; ni < TN; ++ni) {
-        const int col = wn * C::WTN + ni * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-#pragma unroll
-        for (int tq = 0; tq < 4; ++tq) {
-            const int kr = (lane >> 5) * 32 + ((lane & 15) >> 1) + 8 * tq;
-            b_off[ni][tq] = C::B_BASE + ks * BKP * BN + kr * BN + swz_b<BN>(kr, col >> 4) * 16 + (col & 15);
-        }
-    }
-
-    // A slice's LDS reads in a fixed order: q < 2*TM reads half q%2 of A
-    // block q/2, the rest read quarter (q-2TM)%4 of B block (q-2TM)/4.
-    // `abuf` is the LDS address of the slice's A stage; U (slice within the
-    // A stage) and BB (B stage buffer) are compile-time.
-    constexpr int RD = 2 * TM + 4 * TN;
-    auto read_one = [&](auto q_c, auto u_c, auto bb_c, const lds_u8* abuf, Frags<TM, TN>& f) {
-        constexpr int q = decltype(q_c)::value, u = decltype(u_c)::value, bb = decltype(bb_c)::value;
-        if constexpr (q < 2 * TM) {
-            f.a[q / 2][q % 2] = lds_read16(abuf + a_off[u][q / 2][q % 2]);
-        } else {
-            constexpr int qb = q - 2 * TM;
-            f.b[qb / 4][qb % 4] = lds_read_tr8(lds + bb * C::B_STAGE + b_off[qb / 4][qb % 4]);
-        }
-    };
-    auto a_op = [](const Frags<TM, TN>& f, int mi) {
-        const v4i lo = f.a[mi][0], hi = f.a[mi][1];
-        return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    auto b_op = [](const Frags<TM, TN>& f, int ni) {
-        return (v8i){f.b[ni][0][0], f.b[ni][0][1], f.b[ni][1][0], f.b[ni][1][1],
-                     f.b[ni][2][0], f.b[ni][2][1], f.b[ni][3][0], f.b[ni][3][1]};
-    };
-
-    // The slice's matrix instructions in a fixed order.  Fast: one K=64 FP8
-    // MFMA per block, index (mi, ni).  Exact: four K=16 BF16 MFMAs per block;
-    // chunk c (K 32*(l/32) + 8c .. +7 of each lane's bytes, for A and B
-    // alike) feeds MFMAs c*TM*TN .. +TM*TN-1, chunk-outermost so consecutive
-    // MFMAs update different accumulators.  The B fragment is the first
-    // operand, so accumulator block (mi, ni) holds C^T (see TileStore).
-    constexpr int BLK = TM * TN;
-    constexpr int MF = BLK * (EXACT ? 4 : 1);
-    v8bf ab[2][TM], bb[2][TN];  // exact mode: chunk c widened to BF16 in set c & 1
-    auto convert = [&](auto c_c, const Frags<TM, TN>& f) {
-        constexpr int c = decltype(c_c)::value;
-#pragma unroll
-        for (int mi = 0; mi < TM; ++mi) ab[c & 1][mi] = e4m3x8_to_bf16(f.a[mi][c / 2][(c % 2) * 2], f.a[mi][c / 2][(c % 2) * 2 + 1]);
-#pragma unroll
-        for (int ni = 0; ni < TN; ++ni) bb[c & 1][ni] = e4m3x8_to_bf16(f.b[ni][c][0], f.b[ni][c][1]);
-    };
-    auto mfma_one = [&](auto m_c, const Frags<TM, TN>& f) {
-        constexpr int m = decltype(m_c)::value;
-        if constexpr (EXACT) {
-            constexpr int c = m / BLK, mi = (m % BLK) / TN, ni = m % TN;
-            acc[mi][ni] = mfma_32x32x16_bf16(bb[c & 1][ni], ab[c & 1][mi], acc[mi][ni]);
-        } else {
-            constexpr int mi = m / TN, ni = m % TN;
-            acc[mi][ni] = mfma_32x32x64_e4m3(b_op(f, ni), a_op(f, mi), acc[mi][ni]);
-        }
-    };
-
-    // Pipeline (load schedule in PipeLoader).  Slice s, whose fragments are
-    // already in registers or requested:
-    //   wait until the loads of slice s-3 and earlier have landed (the later
-    //   two slices' loads may still be in flight) and this wave's LDS reads
-    //   are complete; barrier -- the stages that slice s+1 reads are visible to
-    //   all waves, and no wave still reads the buffers slice s refills;
-    //   then LPS regions, each: a share of the slice s+1 LDS reads, a share of
-    //   the slice s MFMAs, and one of the slice's LPS loads.
-    // Spreading the loads between the MFMAs keeps the four waves from
-    // queueing a whole stage of loads at once behind the barrier, which
-    // stalls each wave's MFMA issue until the address unit has accepted them.
-    // Loads past the end of K are empty (they read zero), so the body is
-    // branch-free and the in-flight load count is the same every slice.  The
-    // loop is unrolled over the four B buffers (and fragment register pairs);
-    // the slice count is a whole number of A stages, and rounded up to whole
-    // loop bodies, the extra slices multiplying zeros (an accumulator that
-    // starts at +0 stays exact under +0 terms).
-    constexpr int G = C::LPS;  // regions per slice
-    constexpr int U = NBUF_B;  // slices per unrolled body
-    static_assert(U % 2 == 0, "fragment register pairs and A-stage halves alternate");
-    Frags<TM, TN> f0, f1;
-    loader.issue_a_half(-5);
-#pragma unroll
-    for (int s = -4; s < 0; ++s) loader.issue_slice(s);
-    wait_vmcnt_lds<3 * C::LPS>();
-    __syncthreads();
-    static_for<0, RD>([&](auto q_c) {
-        read_one(q_c, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, lds, f0);
-    });
-
-    for (int s0 = 0; s0 < nsteps; s0 += U) {
-        static_for<0, U>([&](auto i_c) {
-            constexpr int i = decltype(i_c)::value;
-            const int s = s0 + i;
-            const Frags<TM, TN>& cur = (i & 1) ? f1 : f0;
-            Frags<TM, TN>& next = (i & 1) ? f0 : f1;
-            wait_vmcnt_lds<2 * C::LPS>();
-            __syncthreads();
-            const typename Loader::Stage stage = loader.prepare(s);
-            // slice s+1: A stage (s+1)/2, slice (i+1)&1 of it; B buffer (i+1)%4
-            const lds_u8* abuf = lds + (((s + 1) >> 1) % NBUF_A) * C::A_STAGE;
-            static_for<0, G>([&](auto r_c) {
-                constexpr int r = decltype(r_c)::value;
-                constexpr int q0 = RD * r / G, q1 = RD * (r + 1) / G;
-                constexpr int m0 = MF * r / G, m1 = MF * (r + 1) / G;
-                if constexpr (EXACT) {
-                    // widen chunk 0 ahead of its MFMAs; chunk c >= 1 one region
-                    // early (in the region holding MFMA c*BLK - 1), so the
-                    // conversions overlap the previous chunk's MFMAs
-                    if constexpr (r == 0) convert(std::integral_constant<int, 0>{}, cur);
-                    static_for<1, 4>([&](auto c_c) {
-                        constexpr int c = decltype(c_c)::value;
-                        if constexpr (c * BLK - 1 >= m0 && c * BLK - 1 < m1) convert(c_c, cur);
-                    });
-                }
-                static_for<q0, q1>([&](auto q_c) {
-                    read_one(q_c, std::integral_constant<int, (i + 1) & 1>{}, std::integral_constant<int, (i + 1) % U>{},
-                             abuf, next);
-                });
-                static_for<m0, m1>([&](auto m_c) { mfma_one(m_c, cur); });
-                // interleave the region's LDS reads with its MFMAs
-                constexpr int nq = q1 - q0, nm = m1 - m0;
-                if constexpr (nm > 0 && nq > 0) {
-                    constexpr int RPM = (nq + nm - 1) / nm;
-#pragma unroll
-                    for (int g = 0; g < (nq + RPM - 1) / RPM; ++g) {
-                        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS read
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                loader.issue_one(stage, r, (i + 1) & 1);
-                __builtin_amdgcn_sched_barrier(0);
-            });
-        });
-    }
-
-    // Drain: the empty tail loads must land before the LDS is reused.
-    wait_vmcnt<0>();
-
-    // Split-K: wave groups 1..KS-1 hand their partial sums to group 0 via LDS.
-    if constexpr (KS > 1) {
-        __syncthreads();
-        float* red = (float*)smem;
-        const int wslot = wm * WN + wn;
-        constexpr int PER = TM * TN * 16 * 64;
-        if (ks > 0) {
-            float* dst = red + ((ks - 1) * WM * WN + wslot) * PER;
-#pragma unroll
-            for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) dst[((mi * TN + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
-        }
-        __syncthreads();
-        if (ks > 0) return;
-#pragma unroll
-        for (int g = 0; g < KS - 1; ++g) {
-            const float* src = red + (g * WM * WN + wslot) * PER;
-#pragma unroll
-            for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < TN; ++ni)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[mi][ni][r] += src[((mi * TN + ni) * 16 + r) * 64 + lane];
-        }
-    }
-
-    // Epilogue: the per-tensor (or per-expert) scale applied once to the sum.
-    // With KS > 1 the LDS scratch sits after the reduction buffer; otherwise
-    // every wave must first be done with the stage buffers.
-    if constexpr (KS == 1) __syncthreads();
-    using Store = TileStore<BF16, TM, TN>;
-    lds_u8* scratch = lds + (KS > 1 ? C::RED : 0) + (wm * WN + wn) * Store::LDS_BYTES;
-    const float scale = p.scale_a[t.expert] * p.scale_b[t.expert];
-    Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch);
-}
-
 template <int BM, int BN, int WM, int WN, int KS, int GROUP_M>
 hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
-    GemmArgs a;
-    a.A = g.A;
-    a.B = g.B;
-    a.C = g.C;
-    a.scale_a = g.scale_a;
-    a.scale_b = g.scale_b;
-    a.offsets = g.offsets;
-    a.experts = g.experts;
-    a.M = g.M;
-    a.N = g.N;
-    a.K = g.K;
-    a.tiles_n = (int32_t)((g.N + BN - 1) / BN);
-    // grouped: an upper bound of sum_e ceil(rows_e / BM); surplus workgroups exit at once
-    a.tiles_m = g.experts == 0 ? (int32_t)((g.M + BM - 1) / BM)
-                               : (int32_t)((g.M + (int64_t)g.experts * (BM - 1)) / BM);
-    const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
-    if (blocks == 0) return hipSuccess;
-    constexpr int NT = 64 * WM * WN * KS;
-    const dim3 grid((unsigned)blocks), block(NT);
-    if (g.fast_acc) {
-        if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, true, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, false, false>), grid, block, 0, s, a);
-    } else {
-        if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, false, true>), grid, block, 0, s, a);
-    }
-    return hipGetLastError();
+    return g.fast_acc ? launch_mode<BM, BN, WM, WN, KS, GROUP_M, MODE_FAST>(g, s)
+                      : launch_mode<BM, BN, WM, WN, KS, GROUP_M, MODE_EXACT>(g, s);
 }
 
 }  // namespace

@@ -1,147 +1,31 @@
-// Block-scaled FP8 GEMM with 32x32 tile scales, for gfx950.
-//
-//   P_kb[m, n] = sum_{k in [32kb, 32kb+32)} A[m, k] * B[k, n]
-//   C[m, n]    = sum_kb s_a[m/32, kb] * s_b[kb, n/32] * P_kb[m, n]
-//
-// The 32x32 scale granularity is the one given in the parameter paragraph of
-// "FP8 GEMM in JAX with Triton for Blackwell"; the scaled partial products
-// are folded into the main FP32 accumulator on the general-purpose ALUs (the
-// "promotion" step the same page assigns to the CUDA cores in its
-// warp-specialisation paragraph).
-//
-// Mapping to CDNA4: a 32x32 MFMA output block coincides with one 32x32 scale
-// tile, so the scale of a K block is a single scalar per MFMA block.  Each K
-// block is reduced by two v_mfma_f32_32x32x16_bf16 (16 K each, fresh zero
-// accumulator) on operands widened exactly from E4M3 to BF16 -- the products
-// are exact, unlike in the FP8 matrix-core forms, whose 8-product groups drop
-// bits more than 13 binades below the group maximum -- and one FMA per
-// accumulator element adds (s_a * s_b) * P_kb into the running FP32 sum.
-// Staging is the same global -> LDS pipeline as the per-tensor kernel.
-#include "gemm_common.h"
-#include "launch.h"
+// Block-scaled FP8 GEMM (32x32 tile scales) for gfx950, over the tile loop of
+// gemm_kernel.h in MODE_BLOCK.  This file is compiled with the MFMA results
+// forced into the architectural VGPRs: the partial products feed the vector
+// FMAs that fold them into the accumulators, which cannot read the
+// accumulation registers directly.
+#include "gemm_kernel.h"
 
 namespace fp8k {
 
-namespace {
-
-template <int BM, int BN, int WM, int WN, int GROUP_M, bool BF16>
-__global__ void __launch_bounds__(64 * WM * WN) gemm_blockscaled_kernel(GemmArgs p) {
-    using C = TileCfg<BM, BN, WM, WN, 1>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
-
-    const TileSlice t = resolve_tile<BM, BN, GROUP_M>(p);
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave / WN;
-    const int wn = wave % WN;
-    const int64_t K = p.K, N = p.N, M = p.M;
-    const int64_t KB = K / 32, NB = N / 32;
-    const int nsteps = (int)((K + BK - 1) / BK);
-    lds_u8* lds = (lds_u8*)smem;
-
-    v16f acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // Scale-tile coordinates of this wave's MFMA blocks (rows/cols beyond M/N
-    // belong to padding and never read a scale).
-    int64_t rb[C::TM], cb[C::TN];
-#pragma unroll
-    for (int mi = 0; mi < C::TM; ++mi) rb[mi] = (t.m0 + wm * C::WTM + mi * 32) / 32;
-#pragma unroll
-    for (int ni = 0; ni < C::TN; ++ni) cb[ni] = (t.n0 + wn * C::WTN + ni * 32) / 32;
-
-    const int h = lane >> 5;
-    const int a_row0 = wm * C::WTM + (lane & 31);
-    const int b_krow0 = h * 16 + ((lane & 15) >> 1);
-    const int b_col0 = wn * C::WTN + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-
-    const StageLoader<BM, BN, WM, WN, 1> loader(t, N, K, wave, lane);
-    if (nsteps > 0) loader.issue(0, lds);
-    for (int step = 0; step < nsteps; ++step) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's stage loads have landed in LDS
-        __syncthreads();                // ... and every wave's; the other buffer is free
-        if (step + 1 < nsteps) loader.issue((int64_t)(step + 1) * BK, lds + ((step + 1) & 1) * C::STAGE);
-        const lds_u8* As = lds + (step & 1) * C::STAGE;
-        const lds_u8* Bs = As + C::A_STAGE;
-#pragma unroll
-        for (int kb = 0; kb < BK / 32; ++kb) {
-            const int64_t kbg = (int64_t)step * (BK / 32) + kb;
-            if (kbg >= KB) break;
-            // lane half h holds K bytes 16h..16h+15 of this block: 8 per MFMA
-            v8bf a_lo[C::TM], a_hi[C::TM], b0[C::TN], b1[C::TN];
-#pragma unroll
-            for (int mi = 0; mi < C::TM; ++mi) {
-                const int row = a_row0 + mi * 32;
-                const v4i v = lds_read16(As + row * BK + swz_a(row, kb * 2 + h) * 16);
-                a_lo[mi] = e4m3x8_to_bf16(v[0], v[1]);
-                a_hi[mi] = e4m3x8_to_bf16(v[2], v[3]);
-            }
-#pragma unroll
-            for (int ni = 0; ni < C::TN; ++ni) {
-                const int col = b_col0 + ni * 32;
-                const int kr0 = kb * 32 + b_krow0;
-                const int kr1 = kr0 + 8;
-                const v2i t0 = lds_read_tr8(Bs + kr0 * BN + swz_b<BN>(kr0, col >> 4) * 16 + (col & 15));
-                const v2i t1 = lds_read_tr8(Bs + kr1 * BN + swz_b<BN>(kr1, col >> 4) * 16 + (col & 15));
-                b0[ni] = e4m3x8_to_bf16(t0[0], t0[1]);
-                b1[ni] = e4m3x8_to_bf16(t1[0], t1[1]);
-            }
-#pragma unroll
-            for (int mi = 0; mi < C::TM; ++mi) {
-                if (rb[mi] * 32 >= M) continue;
-                const float sa = p.scale_a[rb[mi] * KB + kbg];
-#pragma unroll
-                for (int ni = 0; ni < C::TN; ++ni) {
-                    if (cb[ni] * 32 >= N) continue;
-                    const float s = sa * p.scale_b[kbg * NB + cb[ni]];
-                    v16f part = {};
-                    part = mfma_32x32x16_bf16(b0[ni], a_lo[mi], part);  // B first: C^T layout
-                    part = mfma_32x32x16_bf16(b1[ni], a_hi[mi], part);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[mi][ni][r] = fmaf(s, part[r], acc[mi][ni][r]);
-                }
-            }
-        }
-    }
-
-    __syncthreads();  // every wave is done with the stage buffers
-    using Store = TileStore<BF16, C::TM, C::TN>;
-    Store::run(p.C, acc, 1.0f, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, M, N, 0, lane,
-               lds + (wm * WN + wn) * Store::LDS_BYTES);
-}
-
-}  // namespace
-
+// Block-scaled GEMM: 128 x 128 tiles of 4 waves of 64 x 64, whose FP32
+// accumulators and partial products both live in the vector registers the
+// scale folding works on (two workgroups per CU).
 hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,
                                    int64_t M, int64_t N, int64_t K, int32_t out_bf16, hipStream_t s) {
-    constexpr int BM = 128, BN = 128, WM = 2, WN = 2, GROUP_M = 8;
-    GemmArgs a{};
-    a.A = A;
-    a.B = B;
-    a.C = C;
-    a.scale_a = s_a;
-    a.scale_b = s_b;
-    a.offsets = nullptr;
-    a.experts = 0;
-    a.M = M;
-    a.N = N;
-    a.K = K;
-    a.tiles_m = (int32_t)((M + BM - 1) / BM);
-    a.tiles_n = (int32_t)((N + BN - 1) / BN);
-    const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
-    if (blocks == 0) return hipSuccess;
-    if (out_bf16)
-        hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WM, WN, GROUP_M, true>), dim3((unsigned)blocks),
-                           dim3(64 * WM * WN), 0, s, a);
-    else
-        hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WM, WN, GROUP_M, false>), dim3((unsigned)blocks),
-                           dim3(64 * WM * WN), 0, s, a);
-    return hipGetLastError();
+    GemmProblem g{};
+    g.A = A;
+    g.B = B;
+    g.C = C;
+    g.scale_a = s_a;
+    g.scale_b = s_b;
+    g.offsets = nullptr;
+    g.experts = 0;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.out_bf16 = out_bf16;
+    g.fast_acc = 0;
+    return launch_mode<128, 128, 2, 2, 1, 8, MODE_BLOCK>(g, s);
 }
 
 }  // namespace fp8k

@@ -2,26 +2,15 @@
 // FP8 GEMM kernels (per-tensor, grouped and block-scaled).
 //
 // A workgroup owns a BM x BN tile of C.  Its waves form a WM x WN grid of
-// (BM/WM) x (BN/WN) wave tiles made of 32x32 MFMA blocks; KS > 1 splits each
-// K step over KS wave groups.  The K loop moves KS*128 bytes of K per step.
-// Stages go from global memory straight into LDS (buffer_load_dwordx4 ...
-// lds: no VGPR staging), double buffered.  Ragged M/N/K edges use
+// (BM/WM) x (BN/WN) wave tiles made of 32x32 MFMA blocks; KS > 1 splits the
+// K range over KS wave groups.  Stages go from global memory straight into
+// LDS (buffer_load_dwordx4 ... lds: no VGPR staging).  Ragged M/N/K edges use
 // out-of-range buffer offsets, which read as zero without touching memory.
-//
-// LDS layouts, XOR-swizzled at 16-byte granularity:
-//  * A stage: KS sub-tiles of [BM rows][128 bytes of K]; chunk c of row r sits
-//    at position c ^ ((r >> 1) & 7): the 16 rows one ds_read_b128 phase
-//    touches (two rows per 256-byte bank window) land on 16 distinct chunks.
-//  * B stage: KS sub-tiles of [128 K-rows][BN bytes]; rows sharing a 256-byte
-//    window get distinct even XOR masks, so the 8 rows x 2 chunks that one
-//    32-lane phase of ds_read_b64_tr_b8 touches are distinct.
 #pragma once
 
 #include "device_utils.h"
 
 namespace fp8k {
-
-constexpr int BK = 128;  // bytes of K per wave group per step
 
 struct GemmArgs {
     const uint8_t* A;
@@ -35,33 +24,15 @@ struct GemmArgs {
     int32_t tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ int swz_a(int row, int c) { return c ^ ((row >> 1) & 7); }
-
+// B stage layout [K-rows][BN bytes], XOR-swizzled at 16-byte granularity:
+// rows sharing a 256-byte bank window get distinct even XOR masks, so the 8
+// rows x 2 chunks that one phase of ds_read_b64_tr_b8 touches are distinct.
 template <int BN>
 __device__ __forceinline__ int swz_b(int r, int c) {
     constexpr int CPR = BN / 16;                   // chunks per row
     constexpr int RPW = BN >= 256 ? 1 : 256 / BN;  // rows per 256-byte window
     return c ^ (((r / RPW) % (CPR / 2)) * 2);
 }
-
-template <int BM, int BN, int WM, int WN, int KS>
-struct TileCfg {
-    static constexpr int NW = WM * WN * KS;
-    static constexpr int NT = 64 * NW;
-    static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int TM = WTM / 32, TN = WTN / 32;
-    static constexpr int A_STAGE = KS * BM * BK;
-    static constexpr int B_STAGE = KS * BK * BN;
-    static constexpr int STAGE = A_STAGE + B_STAGE;
-    static constexpr int A_INSTR = A_STAGE / 1024;  // wave-wide 1 KiB loads per stage
-    static constexpr int B_INSTR = B_STAGE / 1024;
-    static constexpr int RED = (KS > 1) ? (KS - 1) * BM * BN * 4 : 0;
-    static constexpr int LDS = (2 * STAGE > RED) ? 2 * STAGE : RED;
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "stage loads must split evenly over waves");
-    static_assert(BN >= 64 && BN <= 256 && (BN & (BN - 1)) == 0, "BN must be 64, 128 or 256");
-    static_assert(LDS <= 160 * 1024, "LDS budget");
-};
 
 // The part of the problem one workgroup works on.
 struct TileSlice {
@@ -127,74 +98,6 @@ __device__ __forceinline__ TileSlice resolve_tile(const GemmArgs& p) {
     s.valid = false;
     return s;
 }
-
-// Global -> LDS stage loader.  Every wave issues A_INSTR/NW + B_INSTR/NW
-// wave-wide 1 KiB buffer loads per stage.  The per-lane offsets inside a
-// stage do not change from step to step (the buffer resource's base moves
-// instead), so they are computed once:
-//  * A: slot s of a stage -> (K sub-tile, row, chunk position); the global
-//    chunk is the position XOR-swizzled by the row.  Rows beyond the
-//    problem get the out-of-range offset; a K tail (only in the last step
-//    when K is not a multiple of the step) is masked per load.
-//  * B: slot s -> (sub-tile, K-row, position); columns beyond N get the
-//    out-of-range offset.  The K tail needs no mask: the resource covers
-//    only the (K - k0) remaining rows, so later rows read as zero.
-template <int BM, int BN, int WM, int WN, int KS>
-struct StageLoader {
-    using C = TileCfg<BM, BN, WM, WN, KS>;
-    static constexpr int NA = C::A_INSTR / C::NW, NB = C::B_INSTR / C::NW;
-    uint32_t a_off[NA], b_off[NB];
-    uint32_t a_kk[NA];  // K offset of each A chunk inside the stage
-    const uint8_t* a_base;
-    const uint8_t* b_base;
-    int64_t a_bytes, b_bytes;  // bytes from the bases to the end of each operand
-    int64_t K, N;
-    int wave;
-
-    __device__ __forceinline__ StageLoader(const TileSlice& t, int64_t N_, int64_t K_, int wave_, int lane) {
-        K = K_;
-        N = N_;
-        wave = wave_;
-        const int64_t rows_here = t.M - t.m0;
-        a_base = t.A + t.m0 * K;
-        a_bytes = rows_here * K;
-        b_base = t.B + t.n0;
-        b_bytes = K * N - t.n0;
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int slot = (i * C::NW + wave) * 64 + lane;
-            const int sub = slot / (BM * 8);
-            const int s2 = slot % (BM * 8);
-            const int row = s2 >> 3;
-            const int kk = sub * BK + swz_a(row, s2 & 7) * 16;
-            a_kk[i] = kk;
-            a_off[i] = row < rows_here ? (uint32_t)(row * K + kk) : OOB;
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int slot = (i * C::NW + wave) * 64 + lane;
-            const int sub = slot / (BK * BN / 16);
-            const int s2 = slot % (BK * BN / 16);
-            const int r = s2 / (BN / 16);
-            const int c = swz_b<BN>(r, s2 % (BN / 16));
-            b_off[i] = (t.n0 + c * 16 < N) ? (uint32_t)((sub * BK + r) * N + c * 16) : OOB;
-        }
-    }
-
-    // Enqueue the stage holding K bytes [k0, k0 + KS*128) into LDS at dst.
-    // Branch-free: past the end of K the resources are empty (every load reads
-    // zero), and the K-tail mask is a select.
-    __device__ __forceinline__ void issue(int64_t k0, lds_u8* dst) const {
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + k0, clamp_records(a_bytes - k0));
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + k0 * N, clamp_records(b_bytes - k0 * N));
-        const int64_t krem = K - k0;
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-            load16_to_lds(ra, dst + (i * C::NW + wave) * 1024, (int64_t)a_kk[i] < krem ? a_off[i] : OOB);
-#pragma unroll
-        for (int i = 0; i < NB; ++i) load16_to_lds(rb, dst + C::A_STAGE + (i * C::NW + wave) * 1024, b_off[i]);
-    }
-};
 
 // ---------------------------------------------------------------------------
 // Deep pipeline (per-tensor and grouped GEMM).  The MFMA loop walks slices of

@@ -158,54 +158,90 @@ __device__ __forceinline__ void load_bounds(const int32_t* off, int groups, int6
     __syncthreads();
 }
 
-// Grouped amax: each wave reduces whole rows (cols % 4 == 0) and folds the row
-// max into its group's amax with one atomicMax per row.
-__global__ void __launch_bounds__(kThreads) amax_grouped_kernel(const float* __restrict__ x, int64_t rows, int64_t cols,
-                                                                const int32_t* __restrict__ off, int groups,
-                                                                float* amax) {
-    __shared__ int64_t bnd[1025];
-    load_bounds(off, groups, rows, bnd);
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
-    const int64_t c4 = cols >> 2;
-    for (int64_t r = wave; r < rows; r += nwaves) {
-        const int g = find_group(bnd, groups, r);
-        if (g < 0) continue;
-        const v4f* src = reinterpret_cast<const v4f*>(x + r * cols);
-        float m = 0.0f;
-        for (int64_t j = lane; j < c4; j += 64) {
-            v4f v = __builtin_nontemporal_load(&src[j]);
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+// Grouped kernels: workgroup b owns the contiguous rows [b*rpb, (b+1)*rpb)
+// (rpb = rows per block), its waves take them in turn, and a row is streamed
+// with GQ_U independent 16-byte loads in flight per lane (cols % 4 == 0).
+constexpr int GQ_U = 8;
+
+__device__ __forceinline__ float row_absmax(const v4f* src, int64_t c4, int lane) {
+    float m = 0.0f;
+    for (int64_t j0 = lane; j0 < c4; j0 += 64 * GQ_U) {
+        v4f v[GQ_U];
+#pragma unroll
+        for (int u = 0; u < GQ_U; ++u) {
+            const int64_t j = j0 + u * 64;
+            v[u] = j < c4 ? __builtin_nontemporal_load(&src[j]) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
         }
-        m = wave_max(m);
-        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(amax + g), __float_as_uint(m));
+#pragma unroll
+        for (int u = 0; u < GQ_U; ++u)
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
     }
+    return m;
 }
 
-// Grouped quantize: rows are processed one per wave (lane j takes v4f j,
-// j+64, ...); each row uses its group's scale.  Block 0 also writes scales.
+// Grouped amax: the row maxima of a workgroup meet in a per-group LDS max,
+// and the workgroup then folds each group it touched into the global amax
+// with one atomicMax (on the bit pattern, order-preserving for non-negative
+// floats).
+__global__ void __launch_bounds__(kThreads) amax_grouped_kernel(const float* __restrict__ x, int64_t rows, int64_t cols,
+                                                                const int32_t* __restrict__ off, int groups, int64_t rpb,
+                                                                float* amax) {
+    __shared__ int64_t bnd[1025];
+    __shared__ unsigned int gmax[1024];
+    for (int g = threadIdx.x; g < groups; g += blockDim.x) gmax[g] = 0u;
+    load_bounds(off, groups, rows, bnd);  // ends with a barrier
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r0 = (int64_t)blockIdx.x * rpb;
+    const int64_t r1 = min(r0 + rpb, rows);
+    const int64_t c4 = cols >> 2;
+    for (int64_t r = r0 + wave; r < r1; r += kThreads / 64) {
+        const int g = find_group(bnd, groups, r);
+        if (g < 0) continue;
+        const float m = wave_max(row_absmax(reinterpret_cast<const v4f*>(x + r * cols), c4, lane));
+        if (lane == 0) atomicMax(&gmax[g], __float_as_uint(m));
+    }
+    __syncthreads();
+    // only the groups this workgroup's rows belong to can be non-zero (a zero
+    // needs no atomic: amax starts at zero)
+    for (int g = threadIdx.x; g < groups; g += blockDim.x)
+        if (gmax[g] != 0u) atomicMax(reinterpret_cast<unsigned int*>(amax + g), gmax[g]);
+}
+
+// Grouped quantize: same row partition; each row uses its group's scale.
+// Block 0 also writes the scales.
 __global__ void __launch_bounds__(kThreads) quantize_grouped_kernel(const float* __restrict__ x, int64_t rows,
                                                                     int64_t cols, const int32_t* __restrict__ off,
-                                                                    int groups, const float* __restrict__ amax,
+                                                                    int groups, int64_t rpb,
+                                                                    const float* __restrict__ amax,
                                                                     uint8_t* __restrict__ q, float* scales) {
     __shared__ int64_t bnd[1025];
     load_bounds(off, groups, rows, bnd);
     if (blockIdx.x == 0)
         for (int g = threadIdx.x; g < groups; g += blockDim.x) scales[g] = scale_from_amax(amax[g]);
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r0 = (int64_t)blockIdx.x * rpb;
+    const int64_t r1 = min(r0 + rpb, rows);
     const int64_t c4 = cols >> 2;
-    for (int64_t r = wave; r < rows; r += nwaves) {
+    for (int64_t r = r0 + wave; r < r1; r += kThreads / 64) {
         const int g = find_group(bnd, groups, r);
         if (g < 0) continue;
         const float s = scale_from_amax(amax[g]);
         const v4f* src = reinterpret_cast<const v4f*>(x + r * cols);
         uint32_t* dst = reinterpret_cast<uint32_t*>(q + r * cols);
-        for (int64_t j = lane; j < c4; j += 64) {
-            v4f v = __builtin_nontemporal_load(&src[j]);
-            dst[j] = e4m3x4_sat(__fdiv_rn(v.x, s), __fdiv_rn(v.y, s), __fdiv_rn(v.z, s), __fdiv_rn(v.w, s));
+        for (int64_t j0 = lane; j0 < c4; j0 += 64 * GQ_U) {
+            v4f v[GQ_U];
+#pragma unroll
+            for (int u = 0; u < GQ_U; ++u) {
+                const int64_t j = j0 + u * 64;
+                v[u] = j < c4 ? __builtin_nontemporal_load(&src[j]) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int u = 0; u < GQ_U; ++u) {
+                const int64_t j = j0 + u * 64;
+                if (j < c4)
+                    dst[j] = e4m3x4_sat(__fdiv_rn(v[u].x, s), __fdiv_rn(v[u].y, s), __fdiv_rn(v[u].z, s),
+                                        __fdiv_rn(v[u].w, s));
+            }
         }
     }
 }
@@ -242,12 +278,15 @@ hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, u
 hipError_t launch_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
                                    uint8_t* q, float* scales, float* amax, hipStream_t s) {
     hipLaunchKernelGGL(fill_f32, dim3((groups + 255) / 256), dim3(256), 0, s, amax, groups, 0.0f);
-    const int blocks = stream_blocks(rows, kThreads / 64);
+    // contiguous row runs: up to 2048 workgroups, at least one row each
+    const int64_t nblk = rows < 1 ? 1 : (rows < 2048 ? rows : 2048);
+    const int64_t rpb = rows < 1 ? 1 : (rows + nblk - 1) / nblk;
+    const int blocks = (int)((rows + rpb - 1) / rpb > 0 ? (rows + rpb - 1) / rpb : 1);
     if (rows > 0 && cols > 0)
         hipLaunchKernelGGL(amax_grouped_kernel, dim3(blocks), dim3(kThreads), 0, s, x, rows, cols, offsets, groups,
-                           amax);
+                           rpb, amax);
     hipLaunchKernelGGL(quantize_grouped_kernel, dim3(blocks), dim3(kThreads), 0, s, x, rows, cols, offsets, groups,
-                       (const float*)amax, q, scales);
+                       rpb, (const float*)amax, q, scales);
     return hipGetLastError();
 }
 

@@ -37,72 +37,74 @@ __device__ __forceinline__ void block_max_to(float m, float* dst) {
     }
 }
 
-// amax over n floats (x 16-byte aligned).  Grid-stride over groups of U
-// float4s per thread (U independent 16-byte loads in flight per thread).
-constexpr int AMAX_U = 8;
-__global__ void __launch_bounds__(kThreads) amax_kernel(const float* __restrict__ x, int64_t n, float* amax) {
+// Per-tensor kernels over n floats (x 16-byte aligned).  The n/4 full
+// float4s form chunks of CHUNK4 = 64 * PT_U; workgroup b owns the contiguous
+// chunks [b*cpb, (b+1)*cpb), its waves take them in turn, and a wave streams a
+// chunk with PT_U independent, fully coalesced 16-byte loads per lane in
+// flight.  Workgroup 0 also takes the n % 4 trailing floats.
+constexpr int PT_U = 8;
+constexpr int64_t CHUNK4 = 64 * PT_U;
+
+__global__ void __launch_bounds__(kThreads) amax_kernel(const float* __restrict__ x, int64_t n, int64_t cpb,
+                                                        float* amax) {
     const int64_t n4 = n >> 2;
     const v4f* x4 = reinterpret_cast<const v4f*>(x);
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * cpb;
+    const int64_t c1 = min(c0 + cpb, (n4 + CHUNK4 - 1) / CHUNK4);
     float m = 0.0f;
-    int64_t i = tid;
-    for (; i + (AMAX_U - 1) * stride < n4; i += AMAX_U * stride) {
-        v4f v[AMAX_U];
+    for (int64_t c = c0 + wave; c < c1; c += kThreads / 64) {
+        v4f v[PT_U];
 #pragma unroll
-        for (int u = 0; u < AMAX_U; ++u) v[u] = x4[i + u * stride];
+        for (int u = 0; u < PT_U; ++u) {
+            const int64_t j = c * CHUNK4 + u * 64 + lane;
+            v[u] = j < n4 ? __builtin_nontemporal_load(&x4[j]) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+        }
 #pragma unroll
-        for (int u = 0; u < AMAX_U; ++u)
+        for (int u = 0; u < PT_U; ++u)
             m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
     }
-    for (; i < n4; i += stride) {
-        const v4f v = x4[i];
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-    for (int64_t j = (n4 << 2) + tid; j < n; j += stride) m = fmaxf(m, fabsf(x[j]));
+    if (blockIdx.x == 0)
+        for (int64_t j = (n4 << 2) + threadIdx.x; j < n; j += blockDim.x) m = fmaxf(m, fabsf(x[j]));
     block_max_to(m, amax);
 }
 
-// Codes for n floats with the scale derived from *amax.  Each thread takes
-// QUANT_U groups of 16 consecutive elements per iteration (4 x QUANT_U
-// independent 16-byte loads in flight), one 16-byte code store per group.
-constexpr int QUANT_U = 2;
-__device__ __forceinline__ uint4 quant16(const v4f* src, float s) {
-    v4f v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(&src[j]);
-    uint4 o;
-    o.x = e4m3x4_sat(__fdiv_rn(v[0].x, s), __fdiv_rn(v[0].y, s), __fdiv_rn(v[0].z, s), __fdiv_rn(v[0].w, s));
-    o.y = e4m3x4_sat(__fdiv_rn(v[1].x, s), __fdiv_rn(v[1].y, s), __fdiv_rn(v[1].z, s), __fdiv_rn(v[1].w, s));
-    o.z = e4m3x4_sat(__fdiv_rn(v[2].x, s), __fdiv_rn(v[2].y, s), __fdiv_rn(v[2].z, s), __fdiv_rn(v[2].w, s));
-    o.w = e4m3x4_sat(__fdiv_rn(v[3].x, s), __fdiv_rn(v[3].y, s), __fdiv_rn(v[3].z, s), __fdiv_rn(v[3].w, s));
-    return o;
-}
-
-__global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restrict__ x, int64_t n,
+// Codes for n floats with the scale derived from *amax: the chunk partition
+// of amax_kernel, four codes (one 32-bit store) per float4.
+__global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restrict__ x, int64_t n, int64_t cpb,
                                                             const float* __restrict__ amax, uint8_t* __restrict__ q,
                                                             float* scale_out) {
     const float s = scale_from_amax(*amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
-    const int64_t n16 = n >> 4;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n4 = n >> 2;
     const v4f* x4 = reinterpret_cast<const v4f*>(x);
-    uint4* q16 = reinterpret_cast<uint4*>(q);
-    int64_t i = tid;
-    for (; i + (QUANT_U - 1) * stride < n16; i += QUANT_U * stride) {
-        uint4 o[QUANT_U];
+    uint32_t* q4 = reinterpret_cast<uint32_t*>(q);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * cpb;
+    const int64_t c1 = min(c0 + cpb, (n4 + CHUNK4 - 1) / CHUNK4);
+    for (int64_t c = c0 + wave; c < c1; c += kThreads / 64) {
+        v4f v[PT_U];
 #pragma unroll
-        for (int u = 0; u < QUANT_U; ++u) o[u] = quant16(x4 + 4 * (i + u * stride), s);
+        for (int u = 0; u < PT_U; ++u) {
+            const int64_t j = c * CHUNK4 + u * 64 + lane;
+            v[u] = j < n4 ? __builtin_nontemporal_load(&x4[j]) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+        }
 #pragma unroll
-        for (int u = 0; u < QUANT_U; ++u) q16[i + u * stride] = o[u];
+        for (int u = 0; u < PT_U; ++u) {
+            const int64_t j = c * CHUNK4 + u * 64 + lane;
+            if (j < n4)
+                q4[j] = e4m3x4_sat(__fdiv_rn(v[u].x, s), __fdiv_rn(v[u].y, s), __fdiv_rn(v[u].z, s),
+                                   __fdiv_rn(v[u].w, s));
+        }
     }
-    for (; i < n16; i += stride) q16[i] = quant16(x4 + 4 * i, s);
-    for (int64_t j = (n16 << 4) + tid; j < n; j += stride) q[j] = e4m3_sat(__fdiv_rn(x[j], s));
+    if (blockIdx.x == 0)
+        for (int64_t j = (n4 << 2) + threadIdx.x; j < n; j += blockDim.x) q[j] = e4m3_sat(__fdiv_rn(x[j], s));
 }
 
-// 32x32 tiles: one wave per tile.  Lane l covers row l/2 of the tile, columns
-// 16*(l%2) .. +15: amax over the tile by a wave reduction, then the codes.
+// 32x32 tiles: one wave per tile.  Load j of lane l covers tile row
+// 8j + l/8, columns 4(l%8) .. +3, so each of the four load instructions reads
+// eight whole 128-byte row segments; amax over the tile by a wave reduction,
+// then the codes (a 32-byte run per row and instruction).
 __global__ void __launch_bounds__(kThreads) quantize_blocked_kernel(const float* __restrict__ x, int64_t rows,
                                                                     int64_t cols, uint8_t* __restrict__ q,
                                                                     float* __restrict__ tile_scales) {
@@ -112,24 +114,22 @@ __global__ void __launch_bounds__(kThreads) quantize_blocked_kernel(const float*
     const int64_t tile = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (tile >= ntiles) return;
     const int64_t ti = tile / tiles_c, tj = tile % tiles_c;
-    const int64_t r = ti * 32 + (lane >> 1);
-    const int64_t c = tj * 32 + (lane & 1) * 16;
-    const v4f* src = reinterpret_cast<const v4f*>(x + r * cols + c);
+    const int64_t r = ti * 32 + (lane >> 3);
+    const int64_t c = tj * 32 + (lane & 7) * 4;
     v4f v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(&src[j]);
+    for (int j = 0; j < 4; ++j)
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(x + (r + 8 * j) * cols + c));
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
     m = wave_max(m);
     const float s = scale_from_amax(m);
     if (lane == 0) tile_scales[tile] = s;
-    uint4 o;
-    o.x = e4m3x4_sat(__fdiv_rn(v[0].x, s), __fdiv_rn(v[0].y, s), __fdiv_rn(v[0].z, s), __fdiv_rn(v[0].w, s));
-    o.y = e4m3x4_sat(__fdiv_rn(v[1].x, s), __fdiv_rn(v[1].y, s), __fdiv_rn(v[1].z, s), __fdiv_rn(v[1].w, s));
-    o.z = e4m3x4_sat(__fdiv_rn(v[2].x, s), __fdiv_rn(v[2].y, s), __fdiv_rn(v[2].z, s), __fdiv_rn(v[2].w, s));
-    o.w = e4m3x4_sat(__fdiv_rn(v[3].x, s), __fdiv_rn(v[3].y, s), __fdiv_rn(v[3].z, s), __fdiv_rn(v[3].w, s));
-    *reinterpret_cast<uint4*>(q + r * cols + c) = o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint32_t*>(q + (r + 8 * j) * cols + c) =
+            e4m3x4_sat(__fdiv_rn(v[j].x, s), __fdiv_rn(v[j].y, s), __fdiv_rn(v[j].z, s), __fdiv_rn(v[j].w, s));
 }
 
 // Group of row r by binary search over the (already clamped) boundaries held
@@ -246,22 +246,18 @@ __global__ void __launch_bounds__(kThreads) quantize_grouped_kernel(const float*
     }
 }
 
-int stream_blocks(int64_t work_items, int per_block) {
-    int64_t b = (work_items + per_block - 1) / per_block;
-    if (b < 1) b = 1;
-    if (b > 256 * 16) b = 256 * 16;  // 16 blocks per CU on 256 CUs; grid-stride beyond
-    return (int)b;
-}
-
 }  // namespace
 
 hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, hipStream_t s) {
     hipLaunchKernelGGL(fill_f32, dim3(1), dim3(64), 0, s, amax, 1, 0.0f);
+    // up to 2048 workgroups of contiguous chunks (at least one workgroup)
+    const int64_t nchunks = ((n >> 2) + CHUNK4 - 1) / CHUNK4;
+    const int64_t cpb = nchunks < 2048 ? 1 : (nchunks + 2047) / 2048;
+    const int64_t blocks = nchunks < 1 ? 1 : (nchunks + cpb - 1) / cpb;
     if (n > 0)
-        hipLaunchKernelGGL(amax_kernel, dim3(stream_blocks(n / (4 * AMAX_U) + 1, kThreads)), dim3(kThreads), 0, s, x, n,
-                           amax);
-    hipLaunchKernelGGL(quantize_kernel, dim3(stream_blocks(n / (16 * QUANT_U) + 1, kThreads)), dim3(kThreads), 0, s, x,
-                       n, (const float*)amax, q, scale);
+        hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, n, cpb, amax);
+    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, n, cpb, (const float*)amax, q,
+                       scale);
     return hipGetLastError();
 }
 

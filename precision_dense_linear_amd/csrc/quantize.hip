@@ -58,7 +58,7 @@ __global__ void __launch_bounds__(kThreads) amax_kernel(const float* __restrict_
 #pragma unroll
         for (int u = 0; u < PT_U; ++u) {
             const int64_t j = c * CHUNK4 + u * 64 + lane;
-            v[u] = j < n4 ? __builtin_nontemporal_load(&x4[j]) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+            v[u] = j < n4 ? x4[j] : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
         }
 #pragma unroll
         for (int u = 0; u < PT_U; ++u)
@@ -70,7 +70,10 @@ __global__ void __launch_bounds__(kThreads) amax_kernel(const float* __restrict_
 }
 
 // Codes for n floats with the scale derived from *amax: the chunk partition
-// of amax_kernel, four codes (one 32-bit store) per float4.
+// of amax_kernel, four codes (one 32-bit store) per float4.  amax_kernel
+// reads with ordinary (cache-allocating) loads and this pass walks each
+// workgroup's chunks backwards, so it starts on the lines the first pass
+// touched last, the likeliest to still be in the last-level cache.
 __global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restrict__ x, int64_t n, int64_t cpb,
                                                             const float* __restrict__ amax, uint8_t* __restrict__ q,
                                                             float* scale_out) {
@@ -82,7 +85,7 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restr
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t c0 = (int64_t)blockIdx.x * cpb;
     const int64_t c1 = min(c0 + cpb, (n4 + CHUNK4 - 1) / CHUNK4);
-    for (int64_t c = c0 + wave; c < c1; c += kThreads / 64) {
+    for (int64_t c = c1 - 1 - wave; c >= c0; c -= kThreads / 64) {
         v4f v[PT_U];
 #pragma unroll
         for (int u = 0; u < PT_U; ++u) {

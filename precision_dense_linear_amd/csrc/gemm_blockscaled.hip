@@ -25,7 +25,7 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const flo
     g.K = K;
     g.out_bf16 = out_bf16;
     g.fast_acc = 0;
-    return launch_mode<128, 128, 2, 2, 1, 8, MODE_BLOCK>(g, s);
+    return launch_mode<128, 128, 2, 2, 1, 4, 8, MODE_BLOCK>(g, s);
 }
 
 }  // namespace fp8k

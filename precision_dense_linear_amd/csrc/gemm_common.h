@@ -104,8 +104,9 @@ __device__ __forceinline__ TileSlice resolve_tile(const GemmArgs& p) {
 // 64 bytes of K per wave group.  A is staged 128 bytes of K (two slices) at a
 // time, so every A row of a stage is one whole 128-byte line and each A load
 // is a full-line L2 request; B is staged one slice (64 K-rows of BN bytes,
-// two whole lines per row for BN = 256) at a time.  LDS holds NBUF_A = 3 A
-// stages and then NBUF_B = 4 B stages.
+// two whole lines per row for BN = 256) at a time.  LDS holds NBUF_A A stages
+// and then NB B stages; a deeper pipeline (larger NB) keeps more bytes in
+// flight per workgroup where LDS allows it.
 //  * A stage: KS sub-tiles of [BM rows][128 bytes]; chunk c of row r sits at
 //    position c ^ ((r >> 1) & 7), so the 16 rows of one ds_read_b128 phase
 //    (two rows per 256-byte bank window) hit 16 distinct 16-byte bank groups.
@@ -115,12 +116,13 @@ __device__ __forceinline__ TileSlice resolve_tile(const GemmArgs& p) {
 // ---------------------------------------------------------------------------
 constexpr int BKP = 64;   // bytes of K per slice (one K step of the MFMA loop)
 constexpr int BKA = 128;  // bytes of K per wave group per A stage
-constexpr int NBUF_A = 3, NBUF_B = 4;
 
 __device__ __forceinline__ int swz_a128(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-template <int BM, int BN, int WM, int WN, int KS>
+template <int BM, int BN, int WM, int WN, int KS, int NB_>
 struct PipeCfg {
+    static constexpr int NBUF_B = NB_;               // B stage buffers: NB-1 slices of look-ahead
+    static constexpr int NBUF_A = (NB_ + 2) / 2;     // A stage buffers (two slices each)
     static constexpr int NW = WM * WN * KS;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -136,7 +138,8 @@ struct PipeCfg {
     static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "stage loads must split evenly over waves");
     static_assert(NA % 2 == 0, "an A stage is issued in two halves");
     static_assert(BN >= 64 && BN <= 256 && (BN & (BN - 1)) == 0, "BN must be 64, 128 or 256");
-    static_assert(3 * LPS <= 63, "in-flight loads must fit the vmcnt counter");
+    static_assert(NB_ >= 4 && NB_ % 2 == 0, "B buffers: even, at least 4");
+    static_assert((NB_ - 1) * LPS <= 63, "in-flight loads must fit the vmcnt counter");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -170,14 +173,17 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-// Load schedule: slice s issues B stage s+4 and one half of A stage
-// (s+5)/2 (half (s+1)&1), LPS loads per wave in all.  Stage data is thus
-// issued three slices before the slice whose fragment reads need it, and a
+// Load schedule (NB = NBUF_B): slice s issues B stage s+NB and one half of A
+// stage (s+NB+1)/2 (half (s+1)&1), LPS loads per wave in all.  Stage data is
+// thus issued NB-1 slices before the slice whose fragment reads need it.  A
 // buffer is refilled only after the barrier that follows the reads of its
-// last fragments.
-template <int BM, int BN, int WM, int WN, int KS>
+// last fragments: B stage s+NB goes to the buffer of stage s, whose
+// fragments are in registers by slice s; A stage a is issued from slice
+// 2a-NB-1 into the buffer of stage a-NBUF_A, last read in slice
+// 2(a-NBUF_A) <= 2a-NB-2 because 2*NBUF_A >= NB+2.
+template <int BM, int BN, int WM, int WN, int KS, int NB>
 struct PipeLoader {
-    using C = PipeCfg<BM, BN, WM, WN, KS>;
+    using C = PipeCfg<BM, BN, WM, WN, KS, NB>;
     uint32_t a_off[C::NA], a_kk[C::NA], b_off[C::NB];
     const uint8_t* a_base;
     const uint8_t* b_base;
@@ -224,15 +230,15 @@ struct PipeLoader {
     };
     __device__ __forceinline__ Stage prepare(int s) const {
         Stage g;
-        const int jb = s + NBUF_B;     // B stage
-        const int ja = (s + 5) >> 1;   // A stage
+        const int jb = s + NB;             // B stage
+        const int ja = (s + NB + 1) >> 1;  // A stage
         const int64_t kb0 = (int64_t)(jb >> 1) * (KS * BKA) + (jb & 1) * BKP;
         const int64_t ka0 = (int64_t)ja * (KS * BKA);
         g.ra = make_rsrc(a_base + ka0, clamp_records(a_bytes - ka0));
         g.rb = make_rsrc(b_base + kb0 * N, clamp_records(b_bytes - kb0 * N));
         g.krem = K - ka0;
-        g.dst_a = __builtin_amdgcn_readfirstlane(lds_wave + (uint32_t)(ja % NBUF_A) * C::A_STAGE);
-        g.dst_b = __builtin_amdgcn_readfirstlane(lds_wave + C::B_BASE + (uint32_t)(jb % NBUF_B) * C::B_STAGE);
+        g.dst_a = __builtin_amdgcn_readfirstlane(lds_wave + (uint32_t)(ja % C::NBUF_A) * C::A_STAGE);
+        g.dst_b = __builtin_amdgcn_readfirstlane(lds_wave + C::B_BASE + (uint32_t)(jb % NB) * C::B_STAGE);
         return g;
     }
     // Load r (0 <= r < LPS) of a slice whose A half is `half`: the NB B loads

@@ -62,9 +62,9 @@ enum Mode : int {
     MODE_BLOCK = 2,  // as MODE_EXACT, with a scale pair per 32x32 block and 32-deep K block
 };
 
-template <int BM, int BN, int WM, int WN, int KS, int GROUP_M, bool BF16, int MODE>
+template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, bool BF16, int MODE>
 __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
-    using C = PipeCfg<BM, BN, WM, WN, KS>;
+    using C = PipeCfg<BM, BN, WM, WN, KS, NB>;
     constexpr int TM = C::TM, TN = C::TN;
     constexpr bool WIDEN = MODE != MODE_FAST;
     static_assert(MODE != MODE_BLOCK || KS == 1, "block scales need whole 32-deep K blocks per wave group");
@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     // slices per wave group: whole A stages of KS * 128 bytes of K
     const int nsteps = 2 * (int)((K + KS * BKA - 1) / (KS * BKA));
     lds_u8* lds = (lds_u8*)smem;
-    using Loader = PipeLoader<BM, BN, WM, WN, KS>;
+    using Loader = PipeLoader<BM, BN, WM, WN, KS, NB>;
     const Loader loader(t, N, K, wave, lane, (uint32_t)(uintptr_t)lds);
 
     v16f acc[TM][TN];
@@ -179,27 +179,27 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     };
     // MODE_BLOCK scale indices: tile-scale row of each A block and column of
     // each B block (clamped: blocks past M or N are never stored), and the
-    // number of 32-deep K blocks.
+    // numbers of 32-deep K blocks and 32-wide column blocks.
     int sa_row[TM], sb_col[TN];
-    const int64_t KB = K / 32, NB = N / 32;
+    const int64_t KBLK = K / 32, NBLK = N / 32;
     if constexpr (MODE == MODE_BLOCK) {
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
             sa_row[mi] = (int)min<int64_t>((t.m0 + wm * C::WTM + mi * 32) / 32, t.M / 32 - 1);
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni) sb_col[ni] = (int)min<int64_t>((t.n0 + wn * C::WTN + ni * 32) / 32, NB - 1);
+        for (int ni = 0; ni < TN; ++ni) sb_col[ni] = (int)min<int64_t>((t.n0 + wn * C::WTN + ni * 32) / 32, NBLK - 1);
     }
     // MODE_BLOCK: acc += s_a * s_b * part for accumulator block j, with the
     // scale products sc of the current K block (clamped: past the end of K the
     // partial products are zero).
     float sc[MODE == MODE_BLOCK ? BLK : 1];
     auto load_scales = [&](int64_t kbg) {
-        const int64_t k = min<int64_t>(kbg, KB - 1);
+        const int64_t k = min<int64_t>(kbg, KBLK - 1);
         float sa[TM], sb[TN];
 #pragma unroll
-        for (int mi = 0; mi < TM; ++mi) sa[mi] = p.scale_a[sa_row[mi] * KB + k];
+        for (int mi = 0; mi < TM; ++mi) sa[mi] = p.scale_a[sa_row[mi] * KBLK + k];
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni) sb[ni] = p.scale_b[k * NB + sb_col[ni]];
+        for (int ni = 0; ni < TN; ++ni) sb[ni] = p.scale_b[k * NBLK + sb_col[ni]];
 #pragma unroll
         for (int j = 0; j < BLK; ++j) sc[j] = sa[j / TN] * sb[j % TN];
     };
@@ -210,8 +210,8 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
 
     // Pipeline (load schedule in PipeLoader).  Slice s, whose fragments are
     // already in registers or requested:
-    //   wait until the loads of slice s-3 and earlier have landed (the later
-    //   two slices' loads may still be in flight) and this wave's LDS reads
+    //   wait until the loads of slice s-NB+1 and earlier have landed (the
+    //   later NB-2 slices' loads may still be in flight) and this wave's LDS reads
     //   are complete; barrier -- the stages that slice s+1 reads are visible to
     //   all waves, and no wave still reads the buffers slice s refills;
     //   then G regions, each: a share of the slice s+1 LDS reads, a share of
@@ -222,18 +222,18 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     // In MODE_BLOCK a region is one 32-deep K block: its MFMAs, then the fold.
     // Loads past the end of K are empty (they read zero), so the body is
     // branch-free and the in-flight load count is the same every slice.  The
-    // loop is unrolled over the four B buffers (and fragment register pairs);
+    // loop is unrolled over the NB B buffers (and fragment register pairs);
     // the slice count is a whole number of A stages, and rounded up to whole
     // loop bodies, the extra slices multiplying zeros (an accumulator that
     // starts at +0 stays exact under +0 terms).
     constexpr int G = MODE == MODE_BLOCK ? 2 : C::LPS;  // regions per slice
-    constexpr int U = NBUF_B;                           // slices per unrolled body
+    constexpr int U = NB;                               // slices per unrolled body
     static_assert(U % 2 == 0, "fragment register pairs and A-stage halves alternate");
     Frags<TM, TN> f0, f1;
-    loader.issue_a_half(-5);
+    loader.issue_a_half(-NB - 1);
 #pragma unroll
-    for (int s = -4; s < 0; ++s) loader.issue_slice(s);
-    wait_vmcnt_lds<3 * C::LPS>();
+    for (int s = -NB; s < 0; ++s) loader.issue_slice(s);
+    wait_vmcnt_lds<(NB - 1) * C::LPS>();
     __syncthreads();
     static_for<0, RD>([&](auto q_c) {
         read_one(q_c, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, lds, f0);
@@ -245,11 +245,11 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
             const int s = s0 + i;
             const Frags<TM, TN>& cur = (i & 1) ? f1 : f0;
             Frags<TM, TN>& next = (i & 1) ? f0 : f1;
-            wait_vmcnt_lds<2 * C::LPS>();
+            wait_vmcnt_lds<(NB - 2) * C::LPS>();
             __syncthreads();
             const typename Loader::Stage stage = loader.prepare(s);
-            // slice s+1: A stage (s+1)/2, slice (i+1)&1 of it; B buffer (i+1)%4
-            const lds_u8* abuf = lds + (((s + 1) >> 1) % NBUF_A) * C::A_STAGE;
+            // slice s+1: A stage (s+1)/2, slice (i+1)&1 of it; B buffer (i+1)%NB
+            const lds_u8* abuf = lds + (((s + 1) >> 1) % C::NBUF_A) * C::A_STAGE;
             static_for<0, G>([&](auto r_c) {
                 constexpr int r = decltype(r_c)::value;
                 constexpr int q0 = RD * r / G, q1 = RD * (r + 1) / G;
@@ -266,7 +266,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
                     });
                 }
                 static_for<q0, q1>([&](auto q_c) {
-                    read_one(q_c, std::integral_constant<int, (i + 1) & 1>{}, std::integral_constant<int, (i + 1) % U>{},
+                    read_one(q_c, std::integral_constant<int, (i + 1) & 1>{}, std::integral_constant<int, (i + 1) % NB>{},
                              abuf, next);
                 });
                 constexpr int nq = q1 - q0, nm = m1 - m0;
@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch);
 }
 
-template <int BM, int BN, int WM, int WN, int KS, int GROUP_M, int MODE>
+template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, int MODE>
 hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     GemmArgs a;
     a.A = g.A;
@@ -363,8 +363,8 @@ hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     if (blocks == 0) return hipSuccess;
     constexpr int NT = 64 * WM * WN * KS;
     const dim3 grid((unsigned)blocks), block(NT);
-    if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, true, MODE>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, GROUP_M, false, MODE>), grid, block, 0, s, a);
+    if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NB, GROUP_M, true, MODE>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NB, GROUP_M, false, MODE>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 

@@ -189,23 +189,35 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni) sb_col[ni] = (int)min<int64_t>((t.n0 + wn * C::WTN + ni * 32) / 32, NBLK - 1);
     }
-    // MODE_BLOCK: acc += s_a * s_b * part for accumulator block j, with the
-    // scale products sc of the current K block (clamped: past the end of K the
-    // partial products are zero).
-    float sc[MODE == MODE_BLOCK ? BLK : 1];
-    auto load_scales = [&](int64_t kbg) {
-        const int64_t k = min<int64_t>(kbg, KBLK - 1);
-        float sa[TM], sb[TN];
+    // MODE_BLOCK tile scales: read through the constant address space, so
+    // they come in by scalar loads, counted by lgkmcnt rather than by the
+    // vmcnt that tracks the stage loads, and one slice ahead, so the
+    // lgkmcnt(0) wait at the next slice's barrier covers them.  sa_nx / sb_nx
+    // hold the scales of the next slice's two K blocks (clamped: past the end
+    // of K the partial products are zero).
+    typedef const __attribute__((address_space(4))) float cfloat;
+    float sa_nx[2][TM], sb_nx[2][TN];
+    auto load_slice_scales = [&](int64_t sl) {
 #pragma unroll
-        for (int mi = 0; mi < TM; ++mi) sa[mi] = p.scale_a[sa_row[mi] * KBLK + k];
+        for (int r = 0; r < 2; ++r) {
+            const int64_t k = min<int64_t>(2 * sl + r, KBLK - 1);
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni) sb[ni] = p.scale_b[k * NBLK + sb_col[ni]];
+            for (int mi = 0; mi < TM; ++mi) sa_nx[r][mi] = *(cfloat*)(p.scale_a + sa_row[mi] * KBLK + k);
 #pragma unroll
-        for (int j = 0; j < BLK; ++j) sc[j] = sa[j / TN] * sb[j % TN];
+            for (int ni = 0; ni < TN; ++ni) sb_nx[r][ni] = *(cfloat*)(p.scale_b + k * NBLK + sb_col[ni]);
+        }
     };
-    auto fold_block = [&](int j) {
+    // acc += s_a * s_b * part for every accumulator block, with the scales
+    // (sa, sb) of the K block just multiplied
+    auto fold = [&](const float (&sa)[TM], const float (&sb)[TN]) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[j / TN][j % TN][r] = fmaf(sc[j], part[j / TN][j % TN][r], acc[j / TN][j % TN][r]);
+        for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < TN; ++ni) {
+                const float sc = sa[mi] * sb[ni];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = fmaf(sc, part[mi][ni][r], acc[mi][ni][r]);
+            }
     };
 
     // Pipeline (load schedule in PipeLoader).  Slice s, whose fragments are
@@ -230,6 +242,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     constexpr int U = NB;                               // slices per unrolled body
     static_assert(U % 2 == 0, "fragment register pairs and A-stage halves alternate");
     Frags<TM, TN> f0, f1;
+    if constexpr (MODE == MODE_BLOCK) load_slice_scales(0);
     loader.issue_a_half(-NB - 1);
 #pragma unroll
     for (int s = -NB; s < 0; ++s) loader.issue_slice(s);
@@ -248,6 +261,19 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
             wait_vmcnt_lds<(NB - 2) * C::LPS>();
             __syncthreads();
             const typename Loader::Stage stage = loader.prepare(s);
+            // MODE_BLOCK: this slice's scales (loaded one slice ago), then the
+            // next slice's
+            float sa_cur[2][TM], sb_cur[2][TN];
+            if constexpr (MODE == MODE_BLOCK) {
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+#pragma unroll
+                    for (int mi = 0; mi < TM; ++mi) sa_cur[r][mi] = sa_nx[r][mi];
+#pragma unroll
+                    for (int ni = 0; ni < TN; ++ni) sb_cur[r][ni] = sb_nx[r][ni];
+                }
+                load_slice_scales(s + 1);
+            }
             // slice s+1: A stage (s+1)/2, slice (i+1)&1 of it; B buffer (i+1)%NB
             const lds_u8* abuf = lds + (((s + 1) >> 1) % C::NBUF_A) * C::A_STAGE;
             static_for<0, G>([&](auto r_c) {
@@ -275,11 +301,10 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
                     // partial, then the fold of each block (each depends only
                     // on its own block's last MFMA, so the scheduler can
                     // overlap it with the other blocks' MFMAs)
-                    load_scales(2 * (int64_t)s + r);
                     convert(std::integral_constant<int, 2 * r>{}, cur);
                     convert(std::integral_constant<int, 2 * r + 1>{}, cur);
                     static_for<m0, m1>([&](auto m_c) { mfma_one(m_c, cur); });
-                    static_for<0, BLK>([&](auto j_c) { fold_block(decltype(j_c)::value); });
+                    fold(sa_cur[r], sb_cur[r]);
                 } else {
                     static_for<m0, m1>([&](auto m_c) { mfma_one(m_c, cur); });
                 }

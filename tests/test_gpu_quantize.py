@@ -136,3 +136,23 @@ def test_quantize_grouped_edges():
     check_grouped(x, np.array([0, 10, 10, 33, 50]), "empty group")
     check_grouped(x, np.array([5, 20, 45]), "rows outside the groups")
     check_grouped(x, np.array([0, 50]), "one group")
+
+
+def test_quantize_pertensor_many_chunks_per_workgroup():
+    # 4-float chunks of 512 float4s: a length whose chunk count (6145) exceeds
+    # 2048, so workgroups own several chunks, with a partial last chunk and
+    # 3 trailing floats outside the float4s
+    n = (6144 * 512 + 100) * 4 + 3
+    x = W.gaussian((n,), 2.0, 11, "q-chunks")
+    x[n // 3] = -37.5   # the amax sits in a middle workgroup's range
+    x[n // 3] *= 100.0
+    quantize_and_check(x, "n=%d" % n)
+
+
+def test_quantize_grouped_rows_across_workgroups():
+    # 5000 rows: workgroups own runs of 3 rows (up to 2048 workgroups), so
+    # groups start and end inside runs; ragged column count (9 float4s)
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((5000, 36)) * rng.uniform(0.1, 50.0, (5000, 1))).astype(np.float32)
+    check_grouped(x, np.array([1, 2, 1000, 1000, 1001, 2999, 4998]), "ragged groups across workgroup runs")
+    check_grouped(x, np.array([0, 5000]), "one group over every run")

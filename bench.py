@@ -10,7 +10,13 @@ Printed (rank 0, one JSON line):
                  (TFLOP/s; quantization time included)
   gemm_tflops -- the GEMM kernel alone: 2*M*N*K / its average launch time,
                  measured with HIP events on the launch stream
-  roofline    -- that GEMM kernel against the dense FP8 MFMA peak
+  roofline    -- that GEMM kernel against its roofline: the dense BF16 MFMA
+                 peak for the default (exact-product) kernel, or HBM for the
+                 memory-bound shapes, whose launches are then timed after a
+                 1 GiB read that evicts the last-level cache (B would
+                 otherwise be served from the 256 MB MALL, not HBM)
+  sclk        -- the GPU clock sampled during the timed region, and the
+                 GEMM's fraction of the MFMA peak at that clock
   cpu_baseline-- the CPU oracle timed on a bounded sample of the same step
 Other workloads (--workload) serve profiling of the other shape classes.
 """
@@ -31,6 +37,53 @@ FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (published; 256 CU x 8192 flo
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA (published)
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
+CUS, FP8_FLOP_PER_CU_CLK, BF16_FLOP_PER_CU_CLK = 256, 8192, 4096
+
+
+class SclkSampler:
+    """Polls the current shader clock (the '*' line of pp_dpm_sclk in sysfs)
+    from a background thread; mean_mhz() is None where the file is absent."""
+
+    def __init__(self, period_s: float = 0.002):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for p in self.paths:
+            try:
+                for line in open(p):
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.paths:
+            self._thread.join()
+
+    def mean_mhz(self):
+        # samples at an idle level (under 500 MHz) are gaps between launches
+        busy = [v for v in self.samples if v >= 500.0]
+        return float(np.mean(busy)) if busy else None
 
 
 def csrc_sha256():
@@ -221,14 +274,15 @@ def main():
     # same stream to get the kernel's own average duration.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        w.quantize()
-        ev[i][0].record(stream)
-        w.gemm()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with SclkSampler() as sclk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            w.quantize()
+            ev[i][0].record(stream)
+            w.gemm()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     gemm_ms = [s.elapsed_time(e) for s, e in ev]
 
     # the native-FP8-accumulation GEMM (FP8_ACC_FAST), timed the same way, outside the timed region
@@ -261,6 +315,22 @@ def main():
     avg_gemm_ms = float(np.mean(gemm_ms))
     gemm_tflops = w.flops / (avg_gemm_ms * 1e-3) / 1e12
     mfma_bound = w.flops / w.gemm_bytes() > FP8_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3
+    flushed_ms = None
+    if not mfma_bound:
+        # memory-bound shapes: each launch after a 1 GiB read, which evicts
+        # the 256 MB MALL (where the B codes just written by quantize would
+        # sit) with clean lines, so the launch reads its operands from HBM
+        # and finds no dirty lines to write back first
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        fl = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for s_, e_ in fl:
+            scratch.amax()
+            s_.record(stream)
+            w.gemm()
+            e_.record(stream)
+        torch.cuda.synchronize()
+        flushed_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in fl]))
+        del scratch
     if mfma_bound:
         # the default (exact-product) kernels multiply on the BF16 matrix cores
         peak = BF16_PEAK_TFLOPS
@@ -268,12 +338,21 @@ def main():
                 "frac": round(gemm_tflops / peak, 4), "traffic": measured_traffic(args.workload),
                 "peak_basis": "dense BF16 MFMA: E4M3 operands are widened exactly to BF16 so every product is exact"}
     else:
-        gbps = w.gemm_bytes() / (avg_gemm_ms * 1e-3) / 1e9
+        gbps = w.gemm_bytes() / (flushed_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args.workload)}
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args.workload),
+                "basis": "launches timed after a 1 GiB read that evicts the MALL (operands from HBM)",
+                "in_step_avg_kernel_us": round(avg_gemm_ms * 1e3, 2)}
     roof["kernel"] = "gemm_kernel (fp8_gemm)" if w.kind == "pertensor" else (
-        "gemm_blockscaled_kernel" if w.kind == "block" else "gemm_kernel (fp8_grouped_gemm)")
-    roof["avg_kernel_us"] = round(avg_gemm_ms * 1e3, 2)
+        "gemm_kernel MODE_BLOCK (fp8_gemm_blockscaled)" if w.kind == "block" else "gemm_kernel (fp8_grouped_gemm)")
+    roof["avg_kernel_us"] = round((avg_gemm_ms if mfma_bound else flushed_ms) * 1e3, 2)
+    mhz = sclk.mean_mhz()
+    sclk_out = None
+    if mhz is not None:
+        ghz = mhz / 1e3
+        sclk_out = {"mean_mhz": round(mhz, 1), "samples": len(sclk.samples), "source": "pp_dpm_sclk, timed region",
+                    "gemm_pct_bf16_peak_at_sclk": round(100 * gemm_tflops / (CUS * BF16_FLOP_PER_CU_CLK * ghz / 1e3), 2),
+                    "gemm_pct_fp8_peak_at_sclk": round(100 * gemm_tflops / (CUS * FP8_FLOP_PER_CU_CLK * ghz / 1e3), 2)}
 
     out = {
         "metric": "FP8 GEMM TFLOPS at M=N=K=8192 (BF16 out) + % of MI355X dense FP8 peak",
@@ -295,6 +374,7 @@ def main():
         "quantize_ms": round(q_ms, 4),
         "quantize_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
         "roofline": roof,
+        "sclk": sclk_out,
         "fp8_acc_fast": fast,
         "cpu_baseline": None,
     }

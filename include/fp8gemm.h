@@ -18,9 +18,14 @@
  *   - All matrices are dense and row-major.  E4M3 operands are one byte per
  *     element (OCP FP8 E4M3 "fn": bias 7, max finite 448, 0x7F/0xFF NaN).
  *   - Every pointer argument except `stream` is a DEVICE pointer, allocated
- *     and owned by the caller; the library keeps no state, allocates nothing
- *     and never synchronises with the host.  Scales and offsets live on the
- *     device so that quantize -> GEMM chains need no host round trip.
+ *     and owned by the caller, and the library never synchronises with the
+ *     host.  Scales and offsets live on the device so that quantize -> GEMM
+ *     chains need no host round trip.  The one piece of library state is
+ *     fp8_gemm's split-K workspace (see there): per (device, stream), a
+ *     fixed 16 KiB per CU (4 MiB on 256 CUs) of device memory plus 8 bytes
+ *     of counters per CU, allocated by
+ *     the first call on that stream that splits K and held until the
+ *     process ends.  Nothing else allocates.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued asynchronously on it; results are valid once the
  *     stream has been synchronised.
@@ -127,6 +132,14 @@ fp8_status fp8_quantize_grouped(const float* x, int64_t rows, int64_t cols, cons
  * M, N, K >= 0; K % 16 == 0 and N % 16 == 0 (16-byte rows), K <= 2^23,
  * else FP8_ERR_UNSUPPORTED_SHAPE.  A, B, C 16-byte aligned.  M == 0 or
  * N == 0 enqueues nothing; K == 0 writes zeros.
+ * Split-K: when M <= 64 and the output has too few 32 x 64 tiles to fill
+ * the GPU, the K range is split over up to 8 workgroups per tile; their
+ * FP32 partial sums meet in the stream's workspace and are added in a fixed
+ * order, so results stay deterministic run to run (they may differ in the
+ * last bits from an unsplit sum).  The first such call on a stream
+ * allocates the workspace (hipMalloc may synchronise the device; a call
+ * under stream capture must have been preceded by one outside it); calls
+ * on different streams use different workspaces and may run concurrently.
  */
 fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
                     int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream);

@@ -22,6 +22,13 @@ struct GemmArgs {
     int32_t experts;        // 0 unless grouped
     int64_t M, N, K;
     int32_t tiles_m, tiles_n;
+    // split-K across workgroups (plain GEMM only): `splits` workgroups share a
+    // tile, each over its own K range; their FP32 partials meet in `ws` and
+    // the last to finish (per-tile arrival counters, zero between launches)
+    // sums them in split order and writes C
+    int32_t splits;
+    float* ws;
+    uint32_t* counters;
 };
 
 // B stage layout [K-rows][BN bytes], XOR-swizzled at 16-byte granularity:
@@ -42,19 +49,25 @@ struct TileSlice {
     int64_t m0, n0;     // tile origin inside the problem
     int64_t c_row0;     // row of C that problem row 0 maps to
     int32_t expert;
+    int32_t tile;       // linear tile index (split-K bookkeeping)
+    int32_t split;      // which of the splits of this tile
     bool valid;
 };
 
 // Workgroup id -> tile.  Ids are dealt round-robin over the 8 XCDs, so they
 // are first remapped to give each XCD a contiguous run; runs are then laid
 // out in column bands of GROUP_M tile rows, so that the tiles one XCD works
-// on at the same time share A and B panels in its L2.
+// on at the same time share A and B panels in its L2.  With split-K the
+// `splits` consecutive remapped ids of a tile are its splits.
 template <int BM, int BN, int GROUP_M>
 __device__ __forceinline__ TileSlice resolve_tile(const GemmArgs& p) {
     TileSlice s;
     int bid = blockIdx.x;
     const int nblk = gridDim.x;
     if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+    s.split = bid % p.splits;
+    bid /= p.splits;
+    s.tile = bid;
     const int per_group = GROUP_M * p.tiles_n;
     const int group = bid / per_group;
     const int first_m = group * GROUP_M;
@@ -190,14 +203,16 @@ struct PipeLoader {
     int64_t a_bytes, b_bytes, K, N;
     uint32_t lds_wave;  // LDS byte address of this wave's first 1 KiB slot
 
-    __device__ __forceinline__ PipeLoader(const TileSlice& t, int64_t N_, int64_t K_, int wave, int lane,
-                                          uint32_t lds_base) {
-        K = K_;
+    // Loads K bytes [k_begin, k_end) of the tile's A rows and B columns (the
+    // whole K unless split-K gives this workgroup a part).
+    __device__ __forceinline__ PipeLoader(const TileSlice& t, int64_t N_, int64_t K_, int64_t k_begin, int64_t k_end,
+                                          int wave, int lane, uint32_t lds_base) {
+        K = k_end - k_begin;  // K range this loader covers (A rows keep the full stride K_)
         N = N_;
         const int64_t rows_here = t.M - t.m0;
-        a_base = t.A + t.m0 * K;
-        a_bytes = rows_here * K;
-        b_base = t.B + t.n0;
+        a_base = t.A + t.m0 * K_ + k_begin;
+        a_bytes = rows_here * K_ - k_begin;
+        b_base = t.B + t.n0 + k_begin * N;
         b_bytes = K * N - t.n0;
         lds_wave = lds_base + wave * 1024;
 #pragma unroll
@@ -208,7 +223,7 @@ struct PipeLoader {
             const int row = s2 >> 3;
             const int kk = sub * BKA + swz_a128(row, s2 & 7) * 16;
             a_kk[i] = kk;
-            a_off[i] = row < rows_here ? (uint32_t)(row * K + kk) : OOB;
+            a_off[i] = row < rows_here ? (uint32_t)(row * K_ + kk) : OOB;
         }
 #pragma unroll
         for (int i = 0; i < C::NB; ++i) {

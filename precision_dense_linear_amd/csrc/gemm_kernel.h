@@ -62,7 +62,7 @@ enum Mode : int {
     MODE_BLOCK = 2,  // as MODE_EXACT, with a scale pair per 32x32 block and 32-deep K block
 };
 
-template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, bool BF16, int MODE>
+template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, bool BF16, int MODE, bool SPLITK = false>
 __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     using C = PipeCfg<BM, BN, WM, WN, KS, NB>;
     constexpr int TM = C::TM, TN = C::TN;
@@ -81,11 +81,18 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     const int wm = (wave % (WM * WN)) / WN;
     const int wn = wave % WN;
     const int64_t K = p.K, N = p.N;
-    // slices per wave group: whole A stages of KS * 128 bytes of K
-    const int nsteps = 2 * (int)((K + KS * BKA - 1) / (KS * BKA));
+    // This workgroup's K range: whole A stages (KS * 128 bytes of K), dealt
+    // over the splits of the tile as evenly as they divide (all of K without
+    // split-K; never an empty range while splits <= stages).
+    const int64_t kstep = KS * BKA;
+    const int64_t nkst = (K + kstep - 1) / kstep;
+    const int64_t k_begin = min<int64_t>(t.split * nkst / p.splits * kstep, K);
+    const int64_t k_end = min<int64_t>((t.split + 1) * nkst / p.splits * kstep, K);
+    // slices per wave group: whole A stages
+    const int nsteps = 2 * (int)((k_end - k_begin + kstep - 1) / kstep);
     lds_u8* lds = (lds_u8*)smem;
     using Loader = PipeLoader<BM, BN, WM, WN, KS, NB>;
-    const Loader loader(t, N, K, wave, lane, (uint32_t)(uintptr_t)lds);
+    const Loader loader(t, N, K, k_begin, k_end, wave, lane, (uint32_t)(uintptr_t)lds);
 
     v16f acc[TM][TN];
 #pragma unroll
@@ -343,7 +350,6 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
                     for (int r = 0; r < 16; ++r) dst[((mi * TN + ni) * 16 + r) * 64 + lane] = acc[mi][ni][r];
         }
         __syncthreads();
-        if (ks > 0) return;
 #pragma unroll
         for (int g = 0; g < KS - 1; ++g) {
             const float* src = red + (g * WM * WN + wslot) * PER;
@@ -356,6 +362,69 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
         }
     }
 
+    // Split-K: every split stores its FP32 partial sums (in the lanes' own
+    // layout, coalesced; rows past M skipped) and counts itself in; the last
+    // to arrive sums all the tile's partials in split order -- the same order
+    // whichever split is last, so the result is deterministic -- and writes
+    // C.  Partials and counters are accessed only with device-scope atomics
+    // (coherent across the XCDs' L2s, no whole-cache write-back or
+    // invalidation): a split's stores have completed (vmcnt 0) before it
+    // counts itself in, and the last split reads only after its count came
+    // back.  No workgroup ever waits on another.  (With KS > 1 only wave
+    // group 0 holds the tile's sums; the other groups take part in the
+    // barriers and leave before the epilogue.)
+    if constexpr (SPLITK) {
+        // the flag takes the first LDS word: past the first barrier below no
+        // wave reads the stage or reduction buffers any more
+        int* last_split = reinterpret_cast<int*>(smem);
+        constexpr int PER = TM * TN * 16 * 64;
+        const int wslot = wm * WN + wn;
+        bool row_ok[TM];
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi) row_ok[mi] = t.m0 + wm * C::WTM + mi * 32 + (lane & 31) < t.M;
+        float* mine = p.ws + ((int64_t)(t.tile * p.splits + t.split) * (WM * WN) + wslot) * PER;
+        if (ks == 0) {
+#pragma unroll
+            for (int mi = 0; mi < TM; ++mi)
+                if (row_ok[mi])
+#pragma unroll
+                    for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            __hip_atomic_store(mine + ((mi * TN + ni) * 16 + r) * 64 + lane, acc[mi][ni][r],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            *last_split = __hip_atomic_fetch_add(p.counters + t.tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                          (uint32_t)(p.splits - 1);
+        __syncthreads();
+        if (!*last_split) return;
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+        if (ks == 0) {
+            for (int sp = 0; sp < p.splits; ++sp) {
+                const float* src = p.ws + ((int64_t)(t.tile * p.splits + sp) * (WM * WN) + wslot) * PER;
+#pragma unroll
+                for (int mi = 0; mi < TM; ++mi)
+                    if (row_ok[mi])
+#pragma unroll
+                        for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                acc[mi][ni][r] += __hip_atomic_load(src + ((mi * TN + ni) * 16 + r) * 64 + lane,
+                                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(p.counters + t.tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (ks > 0) return;
+
     // Epilogue: the per-tensor (or per-expert) scale applied once to the sum
     // (block scales are already folded in).  With KS > 1 the LDS scratch sits
     // after the reduction buffer; otherwise every wave must first be done with
@@ -367,8 +436,9 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch);
 }
 
-template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, int MODE>
-hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, int MODE, bool SPLITK = false>
+hipError_t launch_mode(const GemmProblem& g, hipStream_t s, int32_t splits = 1, float* ws = nullptr,
+                       uint32_t* counters = nullptr) {
     GemmArgs a;
     a.A = g.A;
     a.B = g.B;
@@ -384,12 +454,15 @@ hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     // grouped: an upper bound of sum_e ceil(rows_e / BM); surplus workgroups exit at once
     a.tiles_m = g.experts == 0 ? (int32_t)((g.M + BM - 1) / BM)
                                : (int32_t)((g.M + (int64_t)g.experts * (BM - 1)) / BM);
-    const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+    a.splits = SPLITK ? splits : 1;
+    a.ws = ws;
+    a.counters = counters;
+    const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * a.splits;
     if (blocks == 0) return hipSuccess;
     constexpr int NT = 64 * WM * WN * KS;
     const dim3 grid((unsigned)blocks), block(NT);
-    if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NB, GROUP_M, true, MODE>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NB, GROUP_M, false, MODE>), grid, block, 0, s, a);
+    if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NB, GROUP_M, true, MODE, SPLITK>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NB, GROUP_M, false, MODE, SPLITK>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 

@@ -129,6 +129,70 @@ def test_random_ragged_f32(M, N, K):
     pertensor_end_to_end(a, b, F32, what="ragged %dx%dx%d" % (M, N, K))
 
 
+# ------------------------------------------------------------------ split-K
+# M <= 64 with few 32 x 64 tiles splits K over workgroups.  With 256 CUs the
+# shapes below take 2, 8, 4 and 8 splits; the K stage counts (4, 17, 9, 32)
+# give even and uneven K ranges, the last one ending in a partial stage.
+SPLITK_SHAPES = [(1, 512, 1024), (37, 1040, 4112), (64, 2048, 2304), (20, 96, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLITK_SHAPES)
+@pytest.mark.parametrize("fast", [False, True])
+@pytest.mark.parametrize("kind", [F32, BF16])
+def test_splitk_integer_exact_bit_for_bit(M, N, K, fast, kind):
+    """Integer operands make the sum exact in any order, so every split's
+    partial, the fixed-order sum and the ragged row/column edges must give
+    the oracle's value bit for bit."""
+    qa, va = int_codes((M, K), M * 5 + K, lim=8)
+    qb, vb = int_codes((K, N), N * 3 + K, lim=8)
+    C = P.fp8_gemm(gpu(qa), gpu(qb), scalar(1.0), scalar(1.0), torch.float32 if kind == F32 else torch.bfloat16,
+                   fast=fast)
+    bits, exact, _ = oracle.gemm_rows(qa, qb, 1.0, 1.0, kind)
+    got = to_bits(C)
+    assert np.array_equal(got, bits), "%d mismatches" % int((got != bits).sum())
+
+
+@pytest.mark.parametrize("M,N,K", [(48, 3072, 8192), (37, 1040, 4112)])
+def test_splitk_random_f32(M, N, K):
+    a, b = W.pertensor_pair(M, N, K, seed=M * N + K)
+    pertensor_end_to_end(a, b, F32, what="split-K %dx%dx%d" % (M, N, K))
+
+
+def test_splitk_repeated_calls_other_shapes_and_two_streams():
+    """Each launch leaves the per-tile arrival counters at zero: repeated
+    calls, a call with a different tile count in between, and calls on two
+    streams at once (each with its own workspace) give identical bits."""
+    def operands(M, N, K, seed):
+        a, b = W.pertensor_pair(M, N, K, seed=seed)
+        qa, sa, _ = P.fp8_quantize(gpu(a))
+        qb, sb, _ = P.fp8_quantize(gpu(b))
+        return qa, qb, sa, sb
+
+    x = operands(40, 4096, 4096, 3)   # 128 tiles, 4 splits
+    y = operands(16, 1024, 8192, 4)   # 16 tiles, 8 splits
+    Cx = P.fp8_gemm(*x, torch.float32)
+    Cy = P.fp8_gemm(*y, torch.bfloat16)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        assert torch.equal(P.fp8_gemm(*x, torch.float32), Cx)
+        assert torch.equal(P.fp8_gemm(*y, torch.bfloat16).view(torch.int16), Cy.view(torch.int16))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            o1 = P.fp8_gemm(*x, torch.float32)
+        with torch.cuda.stream(s2):
+            o2 = P.fp8_gemm(*y, torch.bfloat16)
+        outs.append((o1, o2))
+    torch.cuda.synchronize()
+    for o1, o2 in outs:
+        assert torch.equal(o1, Cx)
+        assert torch.equal(o2.view(torch.int16), Cy.view(torch.int16))
+    a, b = W.pertensor_pair(40, 4096, 4096, seed=3)
+    pertensor_end_to_end(a, b, F32, what="split-K 40x4096x4096 (oracle)")
+
+
 # ------------------------------------------------------------------ block-scaled
 def blockscaled_end_to_end(a, b, kind, rows=None, what=""):
     qa, ta = P.fp8_quantize_blocked(gpu(a))

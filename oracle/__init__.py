@@ -19,6 +19,12 @@ paragraph -- grouped GEMM over experts):
 * ``gemm_blockscaled_rows`` -- per-32-K-block exact partials, scaled by
                           s_a*s_b and summed in FP64, rounded once.
 * ``grouped_gemm_rows`` -- the per-tensor GEMM applied per expert group.
+* ``e5m2_table``, ``quantize_*_fmt``, ``gemm_rows_fmt`` -- the same for OCP
+                          E5M2 operands (scale = fl32(amax/57344)) and mixed
+                          E4M3 x E5M2 pairs, summed exactly in 128-bit
+                          integers, rounded once to FP32, BF16 or FP16
+                          ("FP8 GEMM in JAX with Triton for Blackwell":
+                          opening section, kernel sketch's float16 store).
 
 The C core lives in ``oracle.c`` and is compiled to ``liboracle.so`` with gcc
 (``build()``); every function there cites the passage it follows.
@@ -36,7 +42,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16 = 0, 1  # output kinds
+F32, BF16, F16 = 0, 1, 2  # output kinds
+E4M3, E5M2 = 0, 1        # operand formats
 
 
 def build(force: bool = True) -> str:
@@ -79,6 +86,21 @@ def lib():
         L.orc_gemm_rows.argtypes = [P, P, f32, f32, i64, i64, P, i64, ctypes.c_int, P, P, P, P]
         L.orc_gemm_sampled.argtypes = [P, P, f32, f32, i64, i64, P, P, i64, ctypes.c_int, P, P, P]
         L.orc_gemm_blockscaled_rows.argtypes = [P, P, P, P, i64, i64, P, i64, ctypes.c_int, P, P, P, P]
+        L.orc_e5m2_decode.restype = ctypes.c_double
+        L.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e5m2_table.argtypes = [P]
+        L.orc_e5m2_rne_sat.restype = ctypes.c_uint8
+        L.orc_e5m2_rne_sat.argtypes = [f32]
+        L.orc_scale_from_amax_fmt.restype = f32
+        L.orc_scale_from_amax_fmt.argtypes = [f32, ctypes.c_int]
+        L.orc_quantize_with_scale_fmt.argtypes = [P, i64, f32, ctypes.c_int, P]
+        L.orc_quantize_pertensor_fmt.argtypes = [P, i64, ctypes.c_int, P, P, P]
+        L.orc_quantize_grouped_fmt.argtypes = [P, i64, P, i32, ctypes.c_int, P, P, P]
+        L.orc_round_ieee_f64.restype = ctypes.c_uint32
+        L.orc_round_ieee_f64.argtypes = [ctypes.c_double, ctypes.c_int]
+        L.orc_gemm_rows_fmt.restype = ctypes.c_int
+        L.orc_gemm_rows_fmt.argtypes = [P, P, ctypes.c_int, ctypes.c_int, f32, f32, i64, i64, P, i64, ctypes.c_int,
+                                        P, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -305,3 +327,88 @@ def grouped_gemm_rows(qx, qw, offsets, scale_x, scale_w, kind, rows=None):
         exact[sel] = x
         sab[sel] = s
     return bits, exact, sab
+
+
+# --------------------------------------------------------------------------
+# Operand formats (E4M3, E5M2) and FP16 output
+# ("FP8 GEMM in JAX with Triton for Blackwell": both FP8 formats on the matrix
+# cores; its kernel sketch stores the accumulator as float16)
+# --------------------------------------------------------------------------
+FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
+
+
+def e5m2_table() -> np.ndarray:
+    """float64[256]: the value of every E5M2 code (+-Inf for 0x7C/0xFC, NaN for 0x7D-0x7F, 0xFD-0xFF)."""
+    out = np.zeros(256, dtype=np.float64)
+    lib().orc_e5m2_table(_p(out))
+    return out
+
+
+def table(fmt: int) -> np.ndarray:
+    return e5m2_table() if fmt == E5M2 else e4m3_table()
+
+
+def e5m2_rne_sat(v: float) -> int:
+    return int(lib().orc_e5m2_rne_sat(ctypes.c_float(v)))
+
+
+def convert_fmt(x: np.ndarray, fmt: int) -> np.ndarray:
+    """Elementwise RNE-saturating FP32 -> codes of the format (scale 1)."""
+    x = _c(x, np.float32)
+    q = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_quantize_with_scale_fmt(_p(x), x.size, ctypes.c_float(1.0), fmt, _p(q))
+    return q
+
+
+def scale_from_amax_fmt(a: float, fmt: int) -> np.float32:
+    return np.float32(lib().orc_scale_from_amax_fmt(ctypes.c_float(a), fmt))
+
+
+def quantize_pertensor_fmt(x: np.ndarray, fmt: int):
+    """Returns (codes, scale, amax) with scale = fl32(amax / format max)."""
+    x = _c(x, np.float32)
+    q = np.empty(x.shape, dtype=np.uint8)
+    s = np.zeros(1, np.float32)
+    a = np.zeros(1, np.float32)
+    lib().orc_quantize_pertensor_fmt(_p(x), x.size, fmt, _p(q), _p(s), _p(a))
+    return q, s[0], a[0]
+
+
+def quantize_grouped_fmt(x: np.ndarray, offsets: np.ndarray, fmt: int):
+    x = _c(x, np.float32)
+    rows, cols = x.shape
+    off = _c(offsets, np.int32)
+    G = off.size - 1
+    q = np.zeros(x.shape, dtype=np.uint8)
+    s = np.empty(G, np.float32)
+    a = np.empty(G, np.float32)
+    lib().orc_quantize_grouped_fmt(_p(x), cols, _p(off), G, fmt, _p(q), _p(s), _p(a))
+    return q, s, a
+
+
+def round_ieee_f64(x: float, kind: int) -> int:
+    """A double rounded once to FP32 / BF16 / FP16 bits (kind F32 / BF16 / F16)."""
+    return int(lib().orc_round_ieee_f64(float(x), kind))
+
+
+def gemm_rows_fmt(qa, qb, fa, fb, sa, sb, kind, rows=None):
+    """Per-tensor scaled GEMM with operand formats fa, fb on the selected rows.
+
+    Returns (bits, exact, sumabs): bits uint32 (FP32) or uint16 (BF16, FP16),
+    rounded once from the exact 128-bit sum; exact = sa*sb*sum_k a*b in FP64;
+    sumabs = sum_k |a*b| (unscaled)."""
+    qa = _c(qa, np.uint8)
+    qb = _c(qb, np.uint8)
+    M, K = qa.shape
+    N = qb.shape[1]
+    assert qb.shape[0] == K
+    rows = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    nr = rows.size
+    out = np.empty((nr, N), np.uint32)
+    exact = np.empty((nr, N), np.float64)
+    sab = np.empty((nr, N), np.float64)
+    st = lib().orc_gemm_rows_fmt(_p(qa), _p(qb), fa, fb, ctypes.c_float(sa), ctypes.c_float(sb), N, K, _p(rows),
+                                 nr, kind, _p(out), _p(exact), _p(sab))
+    if st != 0:
+        raise OverflowError("sum too large for the oracle's 128-bit scaled product")
+    return (out if kind == F32 else out.astype(np.uint16)), exact, sab

@@ -11,7 +11,9 @@
  *   scaling so that values stay inside +-448.
  *   "FP8 GEMM in JAX with Triton for Blackwell" page (2025-10-07), parameter
  *   paragraph: 32x32-block scale granularity ("microscaling"); MoE paragraph:
- *   the grouped GEMM over experts.
+ *   the grouped GEMM over experts; opening section and kernel sketch: the
+ *   E5M2 format beside E4M3, and a float16 store of the accumulator (the
+ *   operand-format and FP16-output variants at the end of this file).
  * Readings where the pages are silent (scale = amax/448, round-to-nearest-even
  * with saturation, division rather than reciprocal, scale applied once after
  * the sum) are listed in the design notes; each function states the one it
@@ -410,4 +412,235 @@ int orc_num_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/* ======================================================================== */
+/* Operand-format and output variants: OCP E5M2 codes, mixed E4M3 x E5M2     */
+/* operands, FP16 output.  "FP8 GEMM in JAX with Triton for Blackwell" page:  */
+/* its opening section names both FP8 formats (E4M3 and E5M2) for the matrix  */
+/* cores, and its kernel sketch stores the FP32 accumulator as float16.       */
+/* Readings (the page gives no more than that): an E5M2 tensor is scaled      */
+/* exactly as an E4M3 one, with E5M2's largest finite value 57344 in place of */
+/* 448 (scale = fl32(amax / 57344), RNE, saturating at +-57344); FP16 output  */
+/* is the IEEE binary16 rounding of the exact scaled sum (nearest-even,       */
+/* subnormals kept, overflow to infinity, as a plain cast does).              */
+/* ======================================================================== */
+
+/* E5M2 ("OCP FP8 E5M2"): sign bit, five exponent bits with bias 15, two
+ * mantissa bits; exponent field 0 holds the subnormals f * 2^-16, field 31
+ * holds +-Inf (mantissa 0) and NaN (mantissa 1..3).  Every finite value is an
+ * integer multiple of 2^-16 no larger than 7 * 2^13 = 57344.  Magnitude of
+ * code m (0 <= m <= 0x7B) in units of 2^-16, straight from the fields:
+ * subnormal f, normal (4 + f) * 2^(e - 1). */
+static int64_t e5m2_mag_x65536(int m) {
+    int e = m >> 2, f = m & 3;
+    return e == 0 ? (int64_t)f : (int64_t)(4 + f) << (e - 1);
+}
+
+/* Signed value of a code in units of 2^-16; Inf and NaN codes report 0 and
+ * *special = 1 (Inf) or 2 (NaN). */
+static int64_t e5m2_x65536(uint8_t c, int* special) {
+    int m = c & 0x7F;
+    if (m >= 0x7C) { if (special) *special = (m == 0x7C) ? 1 : 2; return 0; }
+    if (special) *special = 0;
+    int64_t v = e5m2_mag_x65536(m);
+    return (c & 0x80) ? -v : v;
+}
+
+double orc_e5m2_decode(uint8_t c) {
+    int sp;
+    int64_t v = e5m2_x65536(c, &sp);
+    if (sp == 1) return (c & 0x80) ? -INFINITY : INFINITY;
+    if (sp == 2) return NAN;
+    if (v == 0) return (c & 0x80) ? -0.0 : 0.0;
+    return ldexp((double)v, -16);
+}
+
+void orc_e5m2_table(double* out256) {
+    for (int c = 0; c < 256; c++) out256[c] = orc_e5m2_decode((uint8_t)c);
+}
+
+/* FP32 -> E5M2, round to nearest (ties to the even code), saturating at
+ * +-57344 (Inf included); the sign is kept also when the result is zero; NaN
+ * maps to a NaN code.  The nearest finite value is found by binary search
+ * over the magnitudes of codes 0..0x7B, compared exactly in double. */
+uint8_t orc_e5m2_rne_sat(float v) {
+    if (isnan(v)) return signbit(v) ? 0xFF : 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = ldexp(fabs((double)v), 16);      /* magnitude in units of 2^-16, exact */
+    const int top = 0x7B;
+    if (a >= (double)e5m2_mag_x65536(top)) return sign | (uint8_t)top;
+    int lo = 0, hi = top;                          /* mag[lo] <= a < mag[hi] */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if ((double)e5m2_mag_x65536(mid) <= a) lo = mid; else hi = mid;
+    }
+    double dlo = a - (double)e5m2_mag_x65536(lo);
+    double dup = (double)e5m2_mag_x65536(hi) - a;
+    int pick;
+    if (dlo < dup) pick = lo;
+    else if (dup < dlo) pick = hi;
+    else pick = (lo % 2 == 0) ? lo : hi;
+    return sign | (uint8_t)pick;
+}
+
+/* Format codes: 0 = E4M3, 1 = E5M2. */
+static uint8_t rne_sat_fmt(float v, int fmt) { return fmt ? orc_e5m2_rne_sat(v) : orc_e4m3_rne_sat(v); }
+static float fmt_max(int fmt) { return fmt ? 57344.0f : 448.0f; }
+
+/* scale = amax / (largest finite value of the format), one binary32
+ * division; an all-zero group gets 1. */
+float orc_scale_from_amax_fmt(float amax, int fmt) {
+    if (amax == 0.0f) return 1.0f;
+    volatile float d = fmt_max(fmt);
+    return amax / d;
+}
+
+/* q_i = RNE_SAT_fmt(fl32(x_i / scale)). */
+void orc_quantize_with_scale_fmt(const float* x, int64_t n, float scale, int fmt, uint8_t* q) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        volatile float quot = x[i] / scale;
+        q[i] = rne_sat_fmt(quot, fmt);
+    }
+}
+
+void orc_quantize_pertensor_fmt(const float* x, int64_t n, int fmt, uint8_t* q, float* scale_out, float* amax_out) {
+    float amax = orc_amax(x, n);
+    float s = orc_scale_from_amax_fmt(amax, fmt);
+    orc_quantize_with_scale_fmt(x, n, s, fmt, q);
+    *scale_out = s;
+    *amax_out = amax;
+}
+
+void orc_quantize_grouped_fmt(const float* x, int64_t cols, const int32_t* off, int32_t G, int fmt,
+                              uint8_t* q, float* scales, float* amaxes) {
+    for (int32_t g = 0; g < G; g++) {
+        int64_t r0 = off[g], r1 = off[g + 1];
+        float amax = (r1 > r0) ? orc_amax(x + r0 * cols, (r1 - r0) * cols) : 0.0f;
+        float s = orc_scale_from_amax_fmt(amax, fmt);
+        scales[g] = s;
+        amaxes[g] = amax;
+        if (r1 > r0) orc_quantize_with_scale_fmt(x + r0 * cols, (r1 - r0) * cols, s, fmt, q + r0 * cols);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact rounding to an IEEE binary format with p significand bits (hidden   */
+/* bit included) and an exponent field of `ebits` bits: value = v * 2^e,     */
+/* v a signed 128-bit integer, rounded once to nearest-even; exponent bias   */
+/* 2^(ebits-1) - 1, subnormals below 2^(1 - bias), infinity on overflow.     */
+/* kind 0: binary32 (p 24, 8 bits), 1: bfloat16 (p 8, 8 bits), 2: binary16  */
+/* (p 11, 5 bits).  Returns the bit pattern.                                 */
+/* ------------------------------------------------------------------------ */
+static uint32_t round_ieee(i128 v, int e, int p, int ebits) {
+    const int bias = (1 << (ebits - 1)) - 1;
+    const int emin = 1 - bias;
+    const uint32_t sign = (v < 0) ? (1u << (ebits + p - 1)) : 0u;
+    u128 u = (v < 0) ? (u128)(-v) : (u128)v;
+    if (u == 0) return sign;
+    const int nb = bitlen_u128(u);
+    const int E = nb - 1 + e;                          /* exponent of the leading bit */
+    int lsb = (E < emin ? emin : E) - (p - 1);         /* weight of the last kept bit */
+    const int drop = lsb - e;                          /* low bits of u to drop */
+    u128 mant;
+    if (drop <= 0) {
+        mant = u << (-drop);
+    } else if (drop > nb) {
+        mant = 0;                                      /* below half the smallest step */
+    } else {
+        u128 half = (u128)1 << (drop - 1);
+        u128 rem = (drop == 128) ? u : (u & (((u128)1 << drop) - 1));
+        mant = (drop == 128) ? 0 : (u >> drop);
+        if (rem > half || (rem == half && (mant & 1))) mant += 1;
+    }
+    if (mant == ((u128)1 << p)) { mant >>= 1; lsb += 1; }
+    if (mant >= ((u128)1 << (p - 1))) {                /* normal */
+        const int biased = lsb + p - 1 + bias;
+        if (biased >= (1 << ebits) - 1) return sign | (((1u << ebits) - 1) << (p - 1));
+        return sign | ((uint32_t)biased << (p - 1)) | (uint32_t)(mant - ((u128)1 << (p - 1)));
+    }
+    return sign | (uint32_t)mant;                      /* subnormal */
+}
+
+static void kind_format(int kind, int* p, int* ebits) {
+    if (kind == 0) { *p = 24; *ebits = 8; }
+    else if (kind == 1) { *p = 8; *ebits = 8; }
+    else { *p = 11; *ebits = 5; }
+}
+
+/* A double rounded once to binary32 / bfloat16 / binary16 (kind 0 / 1 / 2). */
+uint32_t orc_round_ieee_f64(double x, int kind) {
+    int p, eb;
+    kind_format(kind, &p, &eb);
+    if (x == 0.0) return signbit(x) ? (1u << (eb + p - 1)) : 0u;
+    int ex;
+    double fr = frexp(x, &ex);
+    int64_t m = (int64_t)ldexp(fr, 53);
+    return round_ieee((i128)m, ex - 53, p, eb);
+}
+
+/* Value of a code in units of 2^-unit (unit 9 for E4M3, 16 for E5M2). */
+static int64_t code_units(uint8_t c, int fmt) {
+    return fmt ? e5m2_x65536(c, 0) : (int64_t)e4m3_x512(c, 0);
+}
+
+/* Per-tensor scaled GEMM with operand formats fa, fb (0 E4M3, 1 E5M2) on a
+ * set of rows of A:
+ *     D[r, j] = sum_k a[rows[r], k] * b[k, j]        exact, as a 128-bit
+ *               integer in units of 2^-(ua + ub) (ua, ub = 9 or 16)
+ *     C[r, j] = round_kind(sa * sb * D[r, j])        one rounding
+ * out receives the bits (kind 0 FP32, 1 BF16, 2 FP16; one uint32 each),
+ * exact the value sa*sb*D in FP64 and sabs sum_k |a*b| (unscaled, FP64).
+ * Returns 0, or -1 if a sum is too large for the 128-bit scaled product (the
+ * products and K at which that can happen are far beyond the workloads). */
+int orc_gemm_rows_fmt(const uint8_t* A, const uint8_t* B, int fa, int fb, float sa, float sb,
+                      int64_t N, int64_t K, const int64_t* rows, int64_t nr, int kind,
+                      uint32_t* out, double* exact, double* sabs) {
+    const int ua = fa ? 16 : 9, ub = fb ? 16 : 9;
+    int64_t ma, mb;
+    int ea, eb;
+    split_f32(sa, &ma, &ea);
+    split_f32(sb, &mb, &eb);
+    const int mbits = bitlen_u128((u128)(ma < 0 ? -ma : ma)) + bitlen_u128((u128)(mb < 0 ? -mb : mb));
+    const double sab_scale = ldexp(1.0, -(ua + ub));
+    int p, ebits;
+    kind_format(kind, &p, &ebits);
+    int status = 0;
+#pragma omp parallel
+    {
+        i128* acc = (i128*)malloc(sizeof(i128) * (size_t)(N > 0 ? N : 1));
+        double* aacc = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nr; r++) {
+            const uint8_t* arow = A + rows[r] * K;
+            for (int64_t j = 0; j < N; j++) { acc[j] = 0; aacc[j] = 0.0; }
+            for (int64_t k = 0; k < K; k++) {
+                const int64_t a = code_units(arow[k], fa);
+                if (a == 0) continue;
+                const uint8_t* brow = B + k * N;
+                for (int64_t j = 0; j < N; j++) {
+                    const i128 prod = (i128)a * (i128)code_units(brow[j], fb);
+                    acc[j] += prod;
+                    aacc[j] += fabs((double)prod);
+                }
+            }
+            for (int64_t j = 0; j < N; j++) {
+                const i128 d = acc[j];
+                const int dbits = bitlen_u128((u128)(d < 0 ? -d : d));
+                if (dbits + mbits > 126) {
+#pragma omp atomic write
+                    status = -1;
+                    out[r * N + j] = 0;
+                } else {
+                    out[r * N + j] = round_ieee((i128)ma * (i128)mb * d, ea + eb - (ua + ub), p, ebits);
+                }
+                exact[r * N + j] = (double)sa * (double)sb * ((double)d * sab_scale);
+                sabs[r * N + j] = aacc[j] * sab_scale;
+            }
+        }
+        free(acc);
+        free(aacc);
+    }
+    return status;
 }

@@ -114,7 +114,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gemm8192",
                     choices=["gemm8192", "gemm1024", "gemm256", "llm16", "llm128", "llm4096", "blockscaled8192",
-                             "moe"])
+                             "moe", "mixed8192"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy twice (reference for the HBM byte counters)")
@@ -135,7 +135,15 @@ class Workload:
         g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         self.kind = "pertensor"
         self.out = torch.bfloat16
-        if name.startswith("gemm"):
+        self.b_e5m2 = False
+        if name == "mixed8192":
+            self.M = self.N = self.K = 8192
+            a, b = W.pertensor_pair(8192, 8192, 8192, seed=0)
+            self.out = torch.float16
+            self.b_e5m2 = True
+            self.desc = ("mixed-format per-tensor FP8 GEMM M=N=K=8192, FP16 out; A FP32 N(0,1) quantized to e4m3fn, "
+                         "B FP32 N(0,1) quantized to e5m2, on device")
+        elif name.startswith("gemm"):
             n = int(name[4:])
             self.M = self.N = self.K = n
             a, b = W.pertensor_pair(n, n, n, seed=0)
@@ -185,7 +193,7 @@ class Workload:
         P = self.P
         if self.kind == "pertensor":
             P.fp8_quantize(self.A, self.qa, self.sa, self.aa)
-            P.fp8_quantize(self.B, self.qb, self.sb, self.ab)
+            (P.fp8_quantize_e5m2 if self.b_e5m2 else P.fp8_quantize)(self.B, self.qb, self.sb, self.ab)
         elif self.kind == "block":
             P.fp8_quantize_blocked(self.A, self.qa, self.sa)
             P.fp8_quantize_blocked(self.B, self.qb, self.sb)
@@ -198,7 +206,8 @@ class Workload:
         qa = self.qa if qa is None else qa
         qb = self.qb if qb is None else qb
         if self.kind == "pertensor":
-            P.fp8_gemm(qa, qb, self.sa, self.sb, self.out, C=self.C, fast=fast)
+            P.fp8_gemm(qa, qb, self.sa, self.sb, self.out, C=self.C, fast=fast,
+                       b_fmt="e5m2" if self.b_e5m2 else "e4m3")
         elif self.kind == "block":
             P.fp8_gemm_blockscaled(qa, qb, self.sa, self.sb, self.out, C=self.C)
         else:
@@ -211,7 +220,7 @@ class Workload:
 
     def gemm_bytes(self):
         """Algorithmic HBM bytes of one GEMM launch: A and B codes once, C once."""
-        osz = 2 if self.out == self.torch.bfloat16 else 4
+        osz = 4 if self.out == self.torch.float32 else 2
         if self.kind == "moe":
             return self.M * self.K + self.E * self.K * self.N + self.M * self.N * osz
         extra = (self.M // 32) * (self.K // 32) * 4 + (self.K // 32) * (self.N // 32) * 4 if self.kind == "block" else 0
@@ -226,7 +235,16 @@ def cpu_baseline(w: Workload, rows: int):
     r = min(rows, M)
     sel = np.arange(r)
     t0 = time.perf_counter()
-    if w.kind == "pertensor":
+    if w.kind == "pertensor" and w.b_e5m2:
+        qa, sa, _ = oracle.quantize_pertensor_fmt(w.a_host[:r], oracle.E4M3)
+        tqa = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        qb, sb, _ = oracle.quantize_pertensor_fmt(w.b_host, oracle.E5M2)
+        tqb = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.gemm_rows_fmt(qa, qb, oracle.E4M3, oracle.E5M2, sa, sb, oracle.F16, rows=sel)
+        tg = time.perf_counter() - t0
+    elif w.kind == "pertensor":
         qa, sa, _ = oracle.quantize_pertensor(w.a_host[:r])
         tqa = time.perf_counter() - t0
         t0 = time.perf_counter()
@@ -240,8 +258,10 @@ def cpu_baseline(w: Workload, rows: int):
     t_step = tqa * M / r + tqb + tg * M / r
     return {"value": round(w.flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "quantize %d of %d rows of A (%.2fs) and all of B (%.2fs), exact FP64 GEMM of those %d rows "
-                      "(%.2fs); scaled to one full step = %.1fs" % (r, M, tqa, tqb, r, tg, t_step)}
+            "sample": "quantize %d of %d rows of A (%.2fs) and all of B (%.2fs), exact %s GEMM of those %d rows "
+                      "(%.2fs); scaled to one full step = %.1fs" % (r, M, tqa, tqb,
+                                                                    "128-bit integer" if w.b_e5m2 else "FP64", r, tg,
+                                                                    t_step)}
 
 
 def main():
@@ -347,7 +367,7 @@ def main():
         peak = BF16_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(gemm_tflops / peak, 4), "traffic": measured_traffic(args.workload),
-                "peak_basis": "dense BF16 MFMA: E4M3 operands are widened exactly to BF16 so every product is exact"}
+                "peak_basis": "dense BF16 MFMA: FP8 operands are widened exactly to BF16 so every product is exact"}
     else:
         gbps = w.gemm_bytes() / (hbm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -376,10 +396,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 (fp32 accumulate)",
+        "dtype": "fp8e4m3 x fp8e5m2 (fp32 accumulate)" if w.b_e5m2 else "fp8e4m3 (fp32 accumulate)",
         "data": "synthetic",
         "config": {"workload": w.desc, "M": w.M, "N": w.N, "K": w.K,
-                   "out": "bf16" if w.out == torch.bfloat16 else "f32", "step": "quantize A and B + GEMM"},
+                   "out": {torch.bfloat16: "bf16", torch.float16: "f16"}.get(w.out, "f32"),
+                   "step": "quantize A and B + GEMM"},
         "gemm_tflops": round(gemm_tflops, 2),
         "gemm_pct_fp8_peak": round(100 * gemm_tflops / FP8_PEAK_TFLOPS, 2),
         "quantize_ms": round(q_ms, 4),

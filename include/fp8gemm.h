@@ -12,11 +12,15 @@
  *   [P3] "FP8 GEMM in JAX with Triton for Blackwell" (blog.hotdry.top,
  *        2025-10-07): parameter paragraph (scale granularity 32x32 blocks),
  *        kernel sketch (row-major A with A[m, k] at m*K + k and B with B[k, n]
- *        at k*N + n), and the MoE paragraph (grouped GEMM over experts).
+ *        at k*N + n; the accumulator stored as float16), the MoE paragraph
+ *        (grouped GEMM over experts), and the opening section (the E4M3 and
+ *        E5M2 FP8 formats on the matrix cores).
  *
  * Conventions for every entry point
- *   - All matrices are dense and row-major.  E4M3 operands are one byte per
- *     element (OCP FP8 E4M3 "fn": bias 7, max finite 448, 0x7F/0xFF NaN).
+ *   - All matrices are dense and row-major.  FP8 operands are one byte per
+ *     element: OCP FP8 E4M3 "fn" (bias 7, max finite 448, 0x7F/0xFF NaN) by
+ *     default, or OCP FP8 E5M2 (bias 15, max finite 57344, 0x7C/0xFC +-Inf,
+ *     0x7D-0x7F/0xFD-0xFF NaN) where the call or a flag says so.
  *   - Every pointer argument except `stream` is a DEVICE pointer, allocated
  *     and owned by the caller, and the library never synchronises with the
  *     host.  Scales and offsets live on the device so that quantize -> GEMM
@@ -56,7 +60,10 @@ typedef enum fp8_status {
 
 typedef enum fp8_out_dtype {
     FP8_OUT_F32 = 0,               /* C is float, 4 bytes per element */
-    FP8_OUT_BF16 = 1               /* C is bfloat16 (round to nearest even), 2 bytes per element */
+    FP8_OUT_BF16 = 1,              /* C is bfloat16 (round to nearest even), 2 bytes per element */
+    FP8_OUT_F16 = 2                /* C is IEEE binary16 ([P3] kernel sketch's float16 store): round to
+                                      nearest even, subnormals kept, overflow to +-Inf; 2 bytes per
+                                      element */
 } fp8_out_dtype;
 
 /*
@@ -81,6 +88,19 @@ typedef enum fp8_out_dtype {
 #define FP8_ACC_FAST 0x100
 
 /*
+ * Operand formats ([P3] opening section: E4M3 and E5M2), OR-ed into the
+ * out_dtype argument of fp8_gemm and fp8_grouped_gemm (not accepted by
+ * fp8_gemm_blockscaled): FP8_A_E5M2 marks A as E5M2 codes, FP8_B_E5M2 marks
+ * B; without them the operand is E4M3.  Every E5M2 value, like every E4M3
+ * value, is a BF16 value, so the default accumulation keeps every product
+ * exact for all four pairs and the FP32 bound above holds unchanged.  With
+ * FP8_ACC_FAST the FP8 matrix cores take the formats per operand, with the
+ * same 8-product grouping.
+ */
+#define FP8_A_E5M2 0x200
+#define FP8_B_E5M2 0x400
+
+/*
  * Per-tensor quantization ([P1] risk paragraph: per-tensor scaling keeps
  * values within the E4M3 range +-448; parameter list: scale_max 448):
  *     amax  = max_i |x_i|
@@ -93,6 +113,16 @@ typedef enum fp8_out_dtype {
  * definition above.
  */
 fp8_status fp8_quantize(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, void* stream);
+
+/*
+ * Per-tensor quantization to E5M2 ([P3] opening section: the E5M2 format;
+ * scaled as in fp8_quantize with E5M2's largest finite value):
+ *     scale = amax / 57344 (one binary32 division; 1.0 when amax == 0)
+ *     q_i   = E5M2(fl32(x_i / scale)), round to nearest even, |v| > 57344
+ *             saturating to +-57344 (codes 0x7B / 0xFB), sign of zero kept.
+ * Arguments, ownership and errors as for fp8_quantize.
+ */
+fp8_status fp8_quantize_e5m2(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, void* stream);
 
 /*
  * 32x32-tile quantization ([P3] parameter paragraph: 32x32 block scale
@@ -122,12 +152,20 @@ fp8_status fp8_quantize_grouped(const float* x, int64_t rows, int64_t cols, cons
                                 int32_t groups, uint8_t* q, float* scales, float* amax, void* stream);
 
 /*
+ * Row-group quantization to E5M2: fp8_quantize_grouped with
+ * scales[g] = amax[g] / 57344 and E5M2 codes as in fp8_quantize_e5m2.
+ */
+fp8_status fp8_quantize_grouped_e5m2(const float* x, int64_t rows, int64_t cols, const int32_t* offsets,
+                                     int32_t groups, uint8_t* q, float* scales, float* amax, void* stream);
+
+/*
  * Per-tensor scaled FP8 GEMM ([P1] kernel section and the paragraph after
  * it; [P3] kernel sketch for the row-major layouts):
  *     C[m, n] = (scale_a * scale_b) * sum_k A[m, k] * B[k, n]
- * with E4M3 products accumulated in FP32 and the scale applied once, after
+ * with FP8 products accumulated in FP32 and the scale applied once, after
  * the K sum.  A: M x K codes, B: K x N codes, C: M x N of out_dtype
- * (FP8_OUT_F32 or FP8_OUT_BF16, optionally OR-ed with FP8_ACC_FAST).
+ * (FP8_OUT_F32, FP8_OUT_BF16 or FP8_OUT_F16, optionally OR-ed with
+ * FP8_ACC_FAST and the operand-format flags FP8_A_E5M2 / FP8_B_E5M2).
  * scale_a, scale_b: one float each on the device.
  * M, N, K >= 0; K % 16 == 0 and N % 16 == 0 (16-byte rows), K <= 2^23,
  * else FP8_ERR_UNSUPPORTED_SHAPE.  A, B, C 16-byte aligned.  M == 0 or
@@ -151,7 +189,8 @@ fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, co
  *     P_kb[m, n] = sum_{k in [32kb, 32kb+32)} A[m, k] * B[k, n]   (FP32)
  *     C[m, n]    = sum_kb s_a[m/32, kb] * s_b[kb, n/32] * P_kb[m, n]
  * accumulated in FP32; each block's partial products are exact (default
- * accumulation mode; FP8_ACC_FAST is not accepted here).
+ * accumulation mode; FP8_ACC_FAST and the operand-format flags are not
+ * accepted here: E4M3 operands only).  C is FP32, BF16 or FP16.
  * s_a: (M/32) x (K/32) floats, s_b: (K/32) x (N/32)
  * floats, row-major, on the device (as written by fp8_quantize_blocked).
  * M, N, K >= 0 and multiples of 32, K <= 2^23, else
@@ -166,8 +205,8 @@ fp8_status fp8_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float*
  * [offsets[e], offsets[e+1]):
  *     C[r, n] = (scale_a[e] * scale_b[e]) * sum_k A[r, k] * B[e, k, n]
  * A: T x K codes (rows grouped by expert), B: experts x K x N codes,
- * C: T x N of out_dtype (with an optional FP8_ACC_FAST flag, as for
- * fp8_gemm); scale_a, scale_b: `experts` floats on the device;
+ * C: T x N of out_dtype (with the optional FP8_ACC_FAST and operand-format
+ * flags, as for fp8_gemm); scale_a, scale_b: `experts` floats on the device;
  * offsets: experts+1 int32 on the device, non-decreasing, clamped to
  * [0, T]; rows outside [offsets[0], offsets[experts]) are left unwritten,
  * and an expert with no rows writes nothing.  1 <= experts <= 1024;

@@ -8,12 +8,16 @@ library's HIP kernels; if the library is missing the import fails.
 
 Entry points (same names as the C ABI):
     fp8_quantize(x)                          -> (q, scale, amax)
+    fp8_quantize_e5m2(x)                     -> (q, scale, amax)
     fp8_quantize_blocked(x)                  -> (q, tile_scales)
     fp8_quantize_grouped(x, offsets)         -> (q, scales, amax)
+    fp8_quantize_grouped_e5m2(x, offsets)    -> (q, scales, amax)
     fp8_gemm(A, B, scale_a, scale_b, out_dtype)
     fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype)
     fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype)
-E4M3 codes are passed as torch.uint8 or torch.float8_e4m3fn tensors.
+FP8 codes are passed as torch.uint8 (E4M3 unless a_fmt / b_fmt say "e5m2"),
+torch.float8_e4m3fn or torch.float8_e5m2 tensors; out_dtype is
+torch.float32, torch.bfloat16 or torch.float16.
 """
 from __future__ import annotations
 
@@ -26,11 +30,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8gemm.so")
 
 FP8_OK, FP8_ERR_INVALID_ARG, FP8_ERR_UNSUPPORTED_SHAPE, FP8_ERR_HIP = 0, 1, 2, 3
-FP8_OUT_F32, FP8_OUT_BF16 = 0, 1
+FP8_OUT_F32, FP8_OUT_BF16, FP8_OUT_F16 = 0, 1, 2
 FP8_ACC_FAST = 0x100  # native FP8 matrix-core accumulation (see include/fp8gemm.h)
+FP8_A_E5M2, FP8_B_E5M2 = 0x200, 0x400  # operand formats (default E4M3)
 
-SYMBOLS = ("fp8_quantize", "fp8_quantize_blocked", "fp8_quantize_grouped", "fp8_gemm",
-           "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_status_string", "fp8_last_error")
+SYMBOLS = ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_grouped",
+           "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
+           "fp8_status_string", "fp8_last_error")
 
 
 class FP8Error(RuntimeError):
@@ -47,13 +53,15 @@ def _load():
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     st = ctypes.c_int
     L.fp8_quantize.argtypes = [P, i64, P, P, P, P]
+    L.fp8_quantize_e5m2.argtypes = [P, i64, P, P, P, P]
     L.fp8_quantize_blocked.argtypes = [P, i64, i64, P, P, P]
     L.fp8_quantize_grouped.argtypes = [P, i64, i64, P, i32, P, P, P, P]
+    L.fp8_quantize_grouped_e5m2.argtypes = [P, i64, i64, P, i32, P, P, P, P]
     L.fp8_gemm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_gemm_blockscaled.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i64, i64, i64, i32, P]
-    for f in ("fp8_quantize", "fp8_quantize_blocked", "fp8_quantize_grouped", "fp8_gemm",
-              "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
+    for f in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_grouped",
+              "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
         getattr(L, f).restype = st
     L.fp8_status_string.restype = ctypes.c_char_p
     L.fp8_status_string.argtypes = [i32]
@@ -79,11 +87,22 @@ def _ptr(t):
 
 
 def _codes(t: torch.Tensor) -> torch.Tensor:
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         return t.view(torch.uint8)
     if t.dtype != torch.uint8:
-        raise TypeError("E4M3 operands must be torch.uint8 or torch.float8_e4m3fn, got %s" % t.dtype)
+        raise TypeError("FP8 operands must be torch.uint8, torch.float8_e4m3fn or torch.float8_e5m2, got %s" % t.dtype)
     return t
+
+
+def _fmt_flag(t: torch.Tensor, fmt, flag: int) -> int:
+    """The operand-format flag of one operand: from an FP8 dtype, else from
+    fmt ("e4m3" / "e5m2", default E4M3)."""
+    from_dtype = {torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}.get(t.dtype)
+    if fmt is None:
+        fmt = from_dtype or "e4m3"
+    _require(fmt in ("e4m3", "e5m2"), "format must be 'e4m3' or 'e5m2', got %r" % (fmt,))
+    _require(from_dtype in (None, fmt), "a %s tensor passed with format %r" % (t.dtype, fmt))
+    return flag if fmt == "e5m2" else 0
 
 
 def _stream(dev: torch.device, stream):
@@ -97,7 +116,9 @@ def _out_code(out_dtype) -> int:
         return FP8_OUT_F32
     if out_dtype in (torch.bfloat16, "bf16", FP8_OUT_BF16):
         return FP8_OUT_BF16
-    raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+    if out_dtype in (torch.float16, "f16", "fp16", FP8_OUT_F16):
+        return FP8_OUT_F16
+    raise ValueError("out_dtype must be torch.float32, torch.bfloat16 or torch.float16")
 
 
 def _require(cond: bool, msg: str):
@@ -105,17 +126,25 @@ def _require(cond: bool, msg: str):
         raise ValueError(msg)
 
 
-def fp8_quantize(x: torch.Tensor, q=None, scale=None, amax=None, stream=None):
-    """Per-tensor E4M3 quantization; returns (q uint8, scale float32[1], amax float32[1])."""
+def _quantize(func: str, x: torch.Tensor, q, scale, amax, stream):
     _require(x.is_cuda and x.dtype == torch.float32 and x.is_contiguous(), "x must be a contiguous float32 GPU tensor")
     dev = x.device
     q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else q
     scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
     amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else amax
     with torch.cuda.device(dev):
-        _check("fp8_quantize", lib.fp8_quantize(_ptr(x), x.numel(), _ptr(q), _ptr(scale), _ptr(amax),
-                                                _stream(dev, stream)))
+        _check(func, getattr(lib, func)(_ptr(x), x.numel(), _ptr(q), _ptr(scale), _ptr(amax), _stream(dev, stream)))
     return q, scale, amax
+
+
+def fp8_quantize(x: torch.Tensor, q=None, scale=None, amax=None, stream=None):
+    """Per-tensor E4M3 quantization; returns (q uint8, scale float32[1], amax float32[1])."""
+    return _quantize("fp8_quantize", x, q, scale, amax, stream)
+
+
+def fp8_quantize_e5m2(x: torch.Tensor, q=None, scale=None, amax=None, stream=None):
+    """Per-tensor E5M2 quantization (scale = amax / 57344); returns (q uint8, scale, amax)."""
+    return _quantize("fp8_quantize_e5m2", x, q, scale, amax, stream)
 
 
 def fp8_quantize_blocked(x: torch.Tensor, q=None, tile_scales=None, stream=None):
@@ -133,8 +162,7 @@ def fp8_quantize_blocked(x: torch.Tensor, q=None, tile_scales=None, stream=None)
     return q, tile_scales
 
 
-def fp8_quantize_grouped(x: torch.Tensor, offsets: torch.Tensor, q=None, scales=None, amax=None, stream=None):
-    """Row-group E4M3 quantization (group g = rows offsets[g]..offsets[g+1]); returns (q, scales, amax)."""
+def _quantize_grouped(func: str, x, offsets, q, scales, amax, stream):
     _require(x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 2,
              "x must be a contiguous 2-D float32 GPU tensor")
     _require(offsets.is_cuda and offsets.dtype == torch.int32, "offsets must be an int32 GPU tensor")
@@ -145,21 +173,35 @@ def fp8_quantize_grouped(x: torch.Tensor, offsets: torch.Tensor, q=None, scales=
     scales = torch.empty(G, dtype=torch.float32, device=dev) if scales is None else scales
     amax = torch.empty(G, dtype=torch.float32, device=dev) if amax is None else amax
     with torch.cuda.device(dev):
-        _check("fp8_quantize_grouped", lib.fp8_quantize_grouped(_ptr(x), rows, cols, _ptr(offsets), G, _ptr(q),
-                                                                _ptr(scales), _ptr(amax), _stream(dev, stream)))
+        _check(func, getattr(lib, func)(_ptr(x), rows, cols, _ptr(offsets), G, _ptr(q), _ptr(scales), _ptr(amax),
+                                        _stream(dev, stream)))
     return q, scales, amax
+
+
+def fp8_quantize_grouped(x: torch.Tensor, offsets: torch.Tensor, q=None, scales=None, amax=None, stream=None):
+    """Row-group E4M3 quantization (group g = rows offsets[g]..offsets[g+1]); returns (q, scales, amax)."""
+    return _quantize_grouped("fp8_quantize_grouped", x, offsets, q, scales, amax, stream)
+
+
+def fp8_quantize_grouped_e5m2(x: torch.Tensor, offsets: torch.Tensor, q=None, scales=None, amax=None, stream=None):
+    """Row-group E5M2 quantization (scales = amax / 57344); returns (q, scales, amax)."""
+    return _quantize_grouped("fp8_quantize_grouped_e5m2", x, offsets, q, scales, amax, stream)
 
 
 def _out_tensor(C, shape, code, dev):
     if C is not None:
         return C
-    return torch.empty(shape, dtype=torch.float32 if code == FP8_OUT_F32 else torch.bfloat16, device=dev)
+    dt = {FP8_OUT_F32: torch.float32, FP8_OUT_BF16: torch.bfloat16, FP8_OUT_F16: torch.float16}[code]
+    return torch.empty(shape, dtype=dt, device=dev)
 
 
-def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=None, fast=False):
-    """C = scale_a*scale_b * A @ B with E4M3 A (M x K) and B (K x N), FP32 accumulation.
+def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=None, fast=False, a_fmt=None,
+             b_fmt=None):
+    """C = scale_a*scale_b * A @ B with FP8 A (M x K) and B (K x N), FP32 accumulation.
 
-    fast=True selects the native FP8 matrix-core accumulation (FP8_ACC_FAST)."""
+    fast=True selects the native FP8 matrix-core accumulation (FP8_ACC_FAST);
+    a_fmt / b_fmt ("e4m3" or "e5m2") give the operand formats of uint8 codes."""
+    flags = _fmt_flag(A, a_fmt, FP8_A_E5M2) | _fmt_flag(B, b_fmt, FP8_B_E5M2) | (FP8_ACC_FAST if fast else 0)
     A, B = _codes(A), _codes(B)
     M, K = A.shape
     N = B.shape[1]
@@ -168,12 +210,13 @@ def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=No
     C = _out_tensor(C, (M, N), code, A.device)
     with torch.cuda.device(A.device):
         _check("fp8_gemm", lib.fp8_gemm(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N, K,
-                                        code | (FP8_ACC_FAST if fast else 0), _stream(A.device, stream)))
+                                        code | flags, _stream(A.device, stream)))
     return C
 
 
 def fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype=torch.bfloat16, C=None, stream=None):
-    """C = sum over 32-wide K blocks of s_a*s_b * (A_kb @ B_kb), 32x32 tile scales."""
+    """C = sum over 32-wide K blocks of s_a*s_b * (A_kb @ B_kb), 32x32 tile scales (E4M3 operands)."""
+    _require(_fmt_flag(A, None, 1) == 0 and _fmt_flag(B, None, 1) == 0, "the block-scaled GEMM takes E4M3 operands")
     A, B = _codes(A), _codes(B)
     M, K = A.shape
     N = B.shape[1]
@@ -186,8 +229,10 @@ def fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype=torch.bfloat16, C=None, strea
     return C
 
 
-def fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=None, fast=False):
+def fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=None, fast=False,
+                     a_fmt=None, b_fmt=None):
     """MoE grouped GEMM: rows offsets[e]..offsets[e+1] of A times B[e], scaled by scale_a[e]*scale_b[e]."""
+    flags = _fmt_flag(A, a_fmt, FP8_A_E5M2) | _fmt_flag(B, b_fmt, FP8_B_E5M2) | (FP8_ACC_FAST if fast else 0)
     A, B = _codes(A), _codes(B)
     T, K = A.shape
     E, K2, N = B.shape
@@ -196,7 +241,6 @@ def fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype=torch.bfloat16, 
     C = _out_tensor(C, (T, N), code, A.device)
     with torch.cuda.device(A.device):
         _check("fp8_grouped_gemm", lib.fp8_grouped_gemm(_ptr(A), _ptr(B), _ptr(offsets), E, _ptr(scale_a),
-                                                        _ptr(scale_b), _ptr(C), T, N, K,
-                                                        code | (FP8_ACC_FAST if fast else 0),
+                                                        _ptr(scale_b), _ptr(C), T, N, K, code | flags,
                                                         _stream(A.device, stream)))
     return C

@@ -42,15 +42,51 @@ fp8_status check_gemm_common(const void* A, const void* B, const void* C, int64_
     // an operand with no elements may be null
     if ((!A && M * K > 0) || (!B && K * N > 0) || (!C && M * N > 0))
         return fail(FP8_ERR_INVALID_ARG, "null matrix pointer");
-    const int32_t base = out_dtype & ~FP8_ACC_FAST;
-    if (base != FP8_OUT_F32 && base != FP8_OUT_BF16)
-        return fail(FP8_ERR_INVALID_ARG, "out_dtype %#x is neither FP8_OUT_F32 nor FP8_OUT_BF16 (| FP8_ACC_FAST)",
+    const int32_t base = out_dtype & 0xFF;
+    if (out_dtype & ~(0xFF | FP8_ACC_FAST | FP8_A_E5M2 | FP8_B_E5M2))
+        return fail(FP8_ERR_INVALID_ARG, "out_dtype %#x has unknown flag bits", out_dtype);
+    if (base != FP8_OUT_F32 && base != FP8_OUT_BF16 && base != FP8_OUT_F16)
+        return fail(FP8_ERR_INVALID_ARG,
+                    "out_dtype %#x is not FP8_OUT_F32, FP8_OUT_BF16 or FP8_OUT_F16 (| FP8_ACC_FAST, FP8_A_E5M2, "
+                    "FP8_B_E5M2)",
                     out_dtype);
     if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return fail(FP8_ERR_INVALID_ARG, "A, B and C must be 16-byte aligned");
     if (K > kMaxK) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld exceeds 2^23", (long long)K);
     if (N > kMaxN) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "N=%lld exceeds 2^20", (long long)N);
     if (M > (int64_t(1) << 31) - 1) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "M=%lld exceeds 2^31-1", (long long)M);
     return FP8_OK;
+}
+
+// The launcher's view of out_dtype: output kind, accumulation mode, formats.
+void decode_out(int32_t out_dtype, fp8k::GemmProblem& g) {
+    const int32_t base = out_dtype & 0xFF;
+    g.out_bf16 = base != FP8_OUT_F32;
+    g.out_f16 = base == FP8_OUT_F16;
+    g.fast_acc = (out_dtype & FP8_ACC_FAST) != 0;
+    g.fmt = ((out_dtype & FP8_A_E5M2) ? 1 : 0) | ((out_dtype & FP8_B_E5M2) ? 2 : 0);
+}
+
+fp8_status quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, int fmt, void* stream,
+                              const char* what) {
+    if (n < 0) return fail(FP8_ERR_INVALID_ARG, "negative n=%lld", (long long)n);
+    if (!scale || !amax || (n > 0 && (!x || !q))) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
+    if (scale == amax) return fail(FP8_ERR_INVALID_ARG, "scale and amax must be distinct");
+    return from_hip(fp8k::launch_quantize_pertensor(x, n, q, scale, amax, fmt, (hipStream_t)stream), what);
+}
+
+fp8_status quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
+                            uint8_t* q, float* scales, float* amax, int fmt, void* stream, const char* what) {
+    if (!x || !q || !scales || !amax || !offsets) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
+    if (rows < 0 || cols < 0) return fail(FP8_ERR_INVALID_ARG, "negative size");
+    if (groups < 1 || groups > 1024) return fail(FP8_ERR_INVALID_ARG, "groups=%d outside [1, 1024]", groups);
+    if (cols % 4) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "cols=%lld must be a multiple of 4", (long long)cols);
+    if (rows > (int64_t(1) << 31) - 1) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "rows exceed 2^31-1");
+    if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
+    if (scales == amax) return fail(FP8_ERR_INVALID_ARG, "scales and amax must be distinct");
+    return from_hip(
+        fp8k::launch_quantize_grouped(x, rows, cols, offsets, groups, q, scales, amax, fmt, (hipStream_t)stream),
+        what);
 }
 
 }  // namespace
@@ -70,11 +106,11 @@ const char* fp8_status_string(int32_t status) {
 const char* fp8_last_error(void) { return g_err; }
 
 fp8_status fp8_quantize(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, void* stream) {
-    if (n < 0) return fail(FP8_ERR_INVALID_ARG, "negative n=%lld", (long long)n);
-    if (!scale || !amax || (n > 0 && (!x || !q))) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
-    if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
-    if (scale == amax) return fail(FP8_ERR_INVALID_ARG, "scale and amax must be distinct");
-    return from_hip(fp8k::launch_quantize_pertensor(x, n, q, scale, amax, (hipStream_t)stream), "fp8_quantize");
+    return quantize_pertensor(x, n, q, scale, amax, 0, stream, "fp8_quantize");
+}
+
+fp8_status fp8_quantize_e5m2(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, void* stream) {
+    return quantize_pertensor(x, n, q, scale, amax, 1, stream, "fp8_quantize_e5m2");
 }
 
 fp8_status fp8_quantize_blocked(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* tile_scales,
@@ -93,15 +129,12 @@ fp8_status fp8_quantize_blocked(const float* x, int64_t rows, int64_t cols, uint
 
 fp8_status fp8_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
                                 uint8_t* q, float* scales, float* amax, void* stream) {
-    if (!x || !q || !scales || !amax || !offsets) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
-    if (rows < 0 || cols < 0) return fail(FP8_ERR_INVALID_ARG, "negative size");
-    if (groups < 1 || groups > 1024) return fail(FP8_ERR_INVALID_ARG, "groups=%d outside [1, 1024]", groups);
-    if (cols % 4) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "cols=%lld must be a multiple of 4", (long long)cols);
-    if (rows > (int64_t(1) << 31) - 1) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "rows exceed 2^31-1");
-    if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
-    if (scales == amax) return fail(FP8_ERR_INVALID_ARG, "scales and amax must be distinct");
-    return from_hip(fp8k::launch_quantize_grouped(x, rows, cols, offsets, groups, q, scales, amax, (hipStream_t)stream),
-                    "fp8_quantize_grouped");
+    return quantize_grouped(x, rows, cols, offsets, groups, q, scales, amax, 0, stream, "fp8_quantize_grouped");
+}
+
+fp8_status fp8_quantize_grouped_e5m2(const float* x, int64_t rows, int64_t cols, const int32_t* offsets,
+                                     int32_t groups, uint8_t* q, float* scales, float* amax, void* stream) {
+    return quantize_grouped(x, rows, cols, offsets, groups, q, scales, amax, 1, stream, "fp8_quantize_grouped_e5m2");
 }
 
 fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
@@ -112,8 +145,8 @@ fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, co
     if (K % 16 || N % 16)
         return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld and N=%lld must be multiples of 16", (long long)K, (long long)N);
     if (M == 0 || N == 0) return ok();
-    fp8k::GemmProblem g{A, B, C, scale_a, scale_b, nullptr, 0, M, N, K,
-                        (out_dtype & ~FP8_ACC_FAST) == FP8_OUT_BF16, (out_dtype & FP8_ACC_FAST) != 0};
+    fp8k::GemmProblem g{A, B, C, scale_a, scale_b, nullptr, 0, M, N, K, 0, 0, 0, 0};
+    decode_out(out_dtype, g);
     return from_hip(fp8k::launch_gemm(g, (hipStream_t)stream), "fp8_gemm");
 }
 
@@ -124,12 +157,13 @@ fp8_status fp8_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float*
     if (!s_a || !s_b) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
     if (out_dtype & FP8_ACC_FAST)
         return fail(FP8_ERR_INVALID_ARG, "FP8_ACC_FAST is not available for the block-scaled GEMM");
+    if (out_dtype & (FP8_A_E5M2 | FP8_B_E5M2))
+        return fail(FP8_ERR_INVALID_ARG, "the block-scaled GEMM takes E4M3 operands only");
     if (M % 32 || N % 32 || K % 32)
         return fail(FP8_ERR_UNSUPPORTED_SHAPE, "M=%lld N=%lld K=%lld must be multiples of 32", (long long)M,
                     (long long)N, (long long)K);
     if (M == 0 || N == 0) return ok();
-    return from_hip(fp8k::launch_gemm_blockscaled(A, B, s_a, s_b, C, M, N, K, out_dtype == FP8_OUT_BF16,
-                                                  (hipStream_t)stream),
+    return from_hip(fp8k::launch_gemm_blockscaled(A, B, s_a, s_b, C, M, N, K, out_dtype & 0xFF, (hipStream_t)stream),
                     "fp8_gemm_blockscaled");
 }
 
@@ -143,8 +177,8 @@ fp8_status fp8_grouped_gemm(const uint8_t* A, const uint8_t* B, const int32_t* o
     if (K % 16 || N % 16)
         return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld and N=%lld must be multiples of 16", (long long)K, (long long)N);
     if (T == 0 || N == 0) return ok();
-    fp8k::GemmProblem g{A, B, C, scale_a, scale_b, offsets, experts, T, N, K,
-                        (out_dtype & ~FP8_ACC_FAST) == FP8_OUT_BF16, (out_dtype & FP8_ACC_FAST) != 0};
+    fp8k::GemmProblem g{A, B, C, scale_a, scale_b, offsets, experts, T, N, K, 0, 0, 0, 0};
+    decode_out(out_dtype, g);
     return from_hip(fp8k::launch_gemm(g, (hipStream_t)stream), "fp8_grouped_gemm");
 }
 

@@ -30,13 +30,16 @@ __device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
     return bytes <= 0 ? 0u : (bytes >= (int64_t)OOB ? OOB : (uint32_t)bytes);
 }
 
-// D = A(32x64) * B(64x32) + C with OCP E4M3 operands, FP32 accumulate
-// (v_mfma_f32_32x32x64_f8f6f4; zero scale operands select the unscaled form).
+// D = A(32x64) * B(64x32) + C with OCP FP8 operands, FP32 accumulate
+// (v_mfma_f32_32x32x64_f8f6f4; zero scale operands select the unscaled
+// form).  The operand formats are given per operand: 0 = E4M3, 1 = E5M2 (the
+// cbsz / blgp fields select the format of the first / second source).
 // Lane l holds A row l%32 / B column l%32, K positions 32*(l/32) .. +31 of
 // the instruction;
 // accumulator element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-__device__ __forceinline__ v16f mfma_32x32x64_e4m3(v8i a, v8i b, v16f c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+template <int FMT_SRC0, int FMT_SRC1>
+__device__ __forceinline__ v16f mfma_32x32x64_f8(v8i a, v8i b, v16f c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT_SRC0, FMT_SRC1, 0, 0, 0, 0);
 }
 
 // D = A(32x16) * B(16x32) + C in BF16 with FP32 accumulate
@@ -58,6 +61,24 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16(int lo, int hi) {
     const v2bf r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)hi, 1.0f, false);
     const v2bf r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)hi, 1.0f, true);
     return (v8bf){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// Eight E5M2 codes -> eight BF16 values, exact as well: every E5M2 value
+// (|v| <= 57344, subnormals down to 2^-16) is a BF16 value
+// (v_cvt_scalef32_pk_bf16_bf8).
+__device__ __forceinline__ v8bf e5m2x8_to_bf16(int lo, int hi) {
+    const v2bf r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((unsigned)lo, 1.0f, false);
+    const v2bf r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((unsigned)lo, 1.0f, true);
+    const v2bf r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((unsigned)hi, 1.0f, false);
+    const v2bf r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((unsigned)hi, 1.0f, true);
+    return (v8bf){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// Eight codes of format F (0 = E4M3, 1 = E5M2) -> eight BF16 values.
+template <int F>
+__device__ __forceinline__ v8bf fp8x8_to_bf16(int lo, int hi) {
+    if constexpr (F == 0) return e4m3x8_to_bf16(lo, hi);
+    else return e5m2x8_to_bf16(lo, hi);
 }
 
 // 8-byte LDS transpose read (ds_read_b64_tr_b8).  Within each 16-lane group,
@@ -105,6 +126,41 @@ __device__ __forceinline__ uint8_t e4m3_sat(float a) {
 // scale = amax / 448 (IEEE binary32 division); 1 for an all-zero group.
 __device__ __forceinline__ float scale_from_amax(float amax) {
     return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+}
+
+// E5M2 counterparts: largest finite value 57344; the clamp keeps values the
+// converter would take past the largest finite value (to Inf) at +-57344.
+__device__ __forceinline__ uint32_t e5m2x4_sat(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, -57344.0f, 57344.0f);
+    b = __builtin_amdgcn_fmed3f(b, -57344.0f, 57344.0f);
+    c = __builtin_amdgcn_fmed3f(c, -57344.0f, 57344.0f);
+    d = __builtin_amdgcn_fmed3f(d, -57344.0f, 57344.0f);
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint8_t e5m2_sat(float a) {
+    a = __builtin_amdgcn_fmed3f(a, -57344.0f, 57344.0f);
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_bf8_f32(a, 0.0f, 0, false) & 0xFF);
+}
+
+// Format-generic forms (F: 0 = E4M3, 1 = E5M2).
+template <int F>
+__device__ __forceinline__ uint32_t fp8x4_sat(float a, float b, float c, float d) {
+    if constexpr (F == 0) return e4m3x4_sat(a, b, c, d);
+    else return e5m2x4_sat(a, b, c, d);
+}
+
+template <int F>
+__device__ __forceinline__ uint8_t fp8_sat(float a) {
+    if constexpr (F == 0) return e4m3_sat(a);
+    else return e5m2_sat(a);
+}
+
+template <int F>
+__device__ __forceinline__ float scale_from_amax_fmt(float amax) {
+    return amax == 0.0f ? 1.0f : __fdiv_rn(amax, F == 0 ? 448.0f : 57344.0f);
 }
 
 }  // namespace fp8k

@@ -1,12 +1,12 @@
-// Per-tensor scaled FP8 GEMM and its MoE grouped form, for gfx950: tile
-// configuration by shape class over the tile loop of gemm_kernel.h, and
-// split-K across workgroups for plain GEMMs with fewer tiles than the GPU
-// has workgroup slots.
+// Per-tensor scaled FP8 GEMM and its MoE grouped form, for gfx950: the
+// E4M3 x E4M3 tile-class dispatch (gemm_dispatch.h), the choice between the
+// operand-format pairs, and the split-K workspace that plain GEMMs with fewer
+// tiles than the GPU has workgroup slots use.
 #include <map>
 #include <mutex>
 #include <utility>
 
-#include "gemm_kernel.h"
+#include "gemm_dispatch.h"
 
 namespace fp8k {
 
@@ -34,13 +34,14 @@ int cu_count() {
 // per tile: 4 MiB at 256 CUs) by the first split-K call on the stream, and
 // kept until the process ends.  The counters are zeroed once, on the stream,
 // when allocated; every launch leaves them at zero again.
-constexpr int64_t SPLIT_TILE_FLOATS = 32 * 64;
 struct SplitWorkspace {
     float* ws = nullptr;
     uint32_t* counters = nullptr;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, SplitWorkspace> g_ws;
+
+}  // namespace
 
 int64_t split_slots() { return 2 * (int64_t)cu_count(); }
 
@@ -83,49 +84,15 @@ int choose_splits(int64_t tiles, int64_t K, int per_cu) {
     return sp;
 }
 
-int64_t tiles_of(int64_t M, int64_t N, int BM, int BN) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+hipError_t launch_gemm_fmt0(const GemmProblem& g, hipStream_t s) { return launch_gemm_t<0>(g, s); }
 
-template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M>
-hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
-    return g.fast_acc ? launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_FAST>(g, s)
-                      : launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_EXACT>(g, s);
-}
-
-// The same tile class with K split `splits` ways across workgroups
-// (tiles * splits <= the workspace's split tiles).
-template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M>
-hipError_t launch_cfg_splitk(const GemmProblem& g, hipStream_t s, int32_t splits) {
-    static_assert(BM * BN == SPLIT_TILE_FLOATS, "workspace sized for this tile");
-    if (tiles_of(g.M, g.N, BM, BN) * splits > split_slots()) return hipErrorInvalidValue;
-    float* ws = nullptr;
-    uint32_t* counters = nullptr;
-    const hipError_t e = get_workspace(s, &ws, &counters);
-    if (e != hipSuccess) return e;
-    return g.fast_acc ? launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_FAST, true>(g, s, splits, ws, counters)
-                      : launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_EXACT, true>(g, s, splits, ws, counters);
-}
-
-}  // namespace
-
-// Tile configuration by shape class (a static table, no runtime tuning):
-//  * M (rows per expert when grouped) <= 64: 32 x 64 tiles with each K step
-//    split over two wave groups -- many workgroups to stream B, HBM bound; a
-//    plain GEMM with fewer such tiles than half the GPU's workgroup slots
-//    also splits K across workgroups (measured on M = 16/32, N = 8192,
-//    K = 8192 with B out of HBM: 36.5 -> 26 us);
-//  * M <= 1024: 128 x 128 tiles, 4 waves of 64 x 64 per K half, the K range
-//    split over two wave groups (more loads in flight per tile);
-//  * larger M: 256 x 256 tiles, 4 waves of 128 x 128 -- MFMA bound.
 hipError_t launch_gemm(const GemmProblem& g, hipStream_t s) {
-    const bool plain = g.experts == 0;
-    const int64_t rows_per_problem = plain ? g.M : (g.M + g.experts - 1) / g.experts;
-    if (rows_per_problem <= 64) {
-        const int sp = plain ? choose_splits(tiles_of(g.M, g.N, 32, 64), g.K, 2) : 1;
-        if (sp > 1) return launch_cfg_splitk<32, 64, 1, 2, 2, 4, 8>(g, s, sp);
-        return launch_cfg<32, 64, 1, 2, 2, 4, 8>(g, s);
+    switch (g.fmt & 3) {
+        case 1: return launch_gemm_fmt1(g, s);
+        case 2: return launch_gemm_fmt2(g, s);
+        case 3: return launch_gemm_fmt3(g, s);
+        default: return launch_gemm_fmt0(g, s);
     }
-    if (rows_per_problem <= 1024) return launch_cfg<128, 128, 2, 2, 2, 4, 8>(g, s);
-    return launch_cfg<256, 256, 2, 2, 1, 4, 8>(g, s);
 }
 
 }  // namespace fp8k

@@ -11,7 +11,7 @@ namespace fp8k {
 // accumulators and partial products both live in the vector registers the
 // scale folding works on (two workgroups per CU).
 hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,
-                                   int64_t M, int64_t N, int64_t K, int32_t out_bf16, hipStream_t s) {
+                                   int64_t M, int64_t N, int64_t K, int32_t out, hipStream_t s) {
     GemmProblem g{};
     g.A = A;
     g.B = B;
@@ -23,8 +23,10 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const flo
     g.M = M;
     g.N = N;
     g.K = K;
-    g.out_bf16 = out_bf16;
+    g.out_bf16 = out != 0;
+    g.out_f16 = out == 2;
     g.fast_acc = 0;
+    g.fmt = 0;
     return launch_mode<128, 128, 2, 2, 1, 4, 8, MODE_BLOCK>(g, s);
 }
 

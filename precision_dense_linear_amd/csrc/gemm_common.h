@@ -29,6 +29,7 @@ struct GemmArgs {
     int32_t splits;
     float* ws;
     uint32_t* counters;
+    int32_t out_f16;  // 2-byte output is IEEE binary16 rather than BF16
 };
 
 // B stage layout [K-rows][BN bytes], XOR-swizzled at 16-byte granularity:
@@ -306,7 +307,7 @@ struct TileStore {
 
     __device__ static __forceinline__ void run(void* C, const v16f (&acc)[TM][TN], float scale, int64_t m_base,
                                                int64_t n_base, int64_t M, int64_t N, int64_t c_row0, int lane,
-                                               lds_u8* scratch) {
+                                               lds_u8* scratch, bool f16) {
         const bool full = (m_base + 32 * TM <= M) && (n_base + 32 * TN <= N);
         const int rows_left = (int)(M - m_base < 32 * TM ? M - m_base : 32 * TM);
         const int cols_left = (int)(N - n_base < 32 * TN ? N - n_base : 32 * TN);
@@ -325,10 +326,17 @@ struct TileStore {
                         const int cb = (ni * 32 + 8 * q + 4 * (lane >> 5)) * OSZ;  // byte column in the row
                         lds_u8* dst = scratch + row * ROWB + swz(row, cb >> 4) * 16 + (cb & 15);
                         if constexpr (BF16) {
-                            typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
-                            const v4bf v = {(__bf16)(a[4 * q] * scale), (__bf16)(a[4 * q + 1] * scale),
-                                            (__bf16)(a[4 * q + 2] * scale), (__bf16)(a[4 * q + 3] * scale)};
-                            *(__attribute__((address_space(3))) v4bf*)dst = v;
+                            if (f16) {
+                                typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+                                const v4h v = {(_Float16)(a[4 * q] * scale), (_Float16)(a[4 * q + 1] * scale),
+                                               (_Float16)(a[4 * q + 2] * scale), (_Float16)(a[4 * q + 3] * scale)};
+                                *(__attribute__((address_space(3))) v4h*)dst = v;
+                            } else {
+                                typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+                                const v4bf v = {(__bf16)(a[4 * q] * scale), (__bf16)(a[4 * q + 1] * scale),
+                                                (__bf16)(a[4 * q + 2] * scale), (__bf16)(a[4 * q + 3] * scale)};
+                                *(__attribute__((address_space(3))) v4bf*)dst = v;
+                            }
                         } else {
                             const v4f v = {a[4 * q] * scale, a[4 * q + 1] * scale, a[4 * q + 2] * scale,
                                            a[4 * q + 3] * scale};

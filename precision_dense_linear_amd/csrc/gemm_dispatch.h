@@ -1,0 +1,62 @@
+// Tile-class dispatch of the per-tensor and grouped FP8 GEMM, for one
+// operand-format pair FMT (bit 0: A holds E5M2 codes, bit 1: B; else E4M3).
+// Each format pair is instantiated in a translation unit of its own
+// (gemm.hip, gemm_fmt1.hip, gemm_fmt2.hip, gemm_fmt3.hip).
+#pragma once
+
+#include "gemm_kernel.h"
+
+namespace fp8k {
+
+// Split-K workspace and split choice (gemm.hip).
+constexpr int64_t SPLIT_TILE_FLOATS = 32 * 64;
+int64_t split_slots();
+hipError_t get_workspace(hipStream_t s, float** ws, uint32_t** counters);
+int choose_splits(int64_t tiles, int64_t K, int per_cu);
+
+inline int64_t tiles_of(int64_t M, int64_t N, int BM, int BN) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+
+template <int FMT, int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M>
+hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
+    return g.fast_acc ? launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_FAST, false, FMT>(g, s)
+                      : launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_EXACT, false, FMT>(g, s);
+}
+
+// The same tile class with K split `splits` ways across workgroups
+// (tiles * splits <= the workspace's split tiles).
+template <int FMT, int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M>
+hipError_t launch_cfg_splitk(const GemmProblem& g, hipStream_t s, int32_t splits) {
+    static_assert(BM * BN == SPLIT_TILE_FLOATS, "workspace sized for this tile");
+    if (tiles_of(g.M, g.N, BM, BN) * splits > split_slots()) return hipErrorInvalidValue;
+    float* ws = nullptr;
+    uint32_t* counters = nullptr;
+    const hipError_t e = get_workspace(s, &ws, &counters);
+    if (e != hipSuccess) return e;
+    return g.fast_acc
+               ? launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_FAST, true, FMT>(g, s, splits, ws, counters)
+               : launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_EXACT, true, FMT>(g, s, splits, ws, counters);
+}
+
+// Tile configuration by shape class (a static table, no runtime tuning):
+//  * M (rows per expert when grouped) <= 64: 32 x 64 tiles with each K step
+//    split over two wave groups -- many workgroups to stream B, HBM bound; a
+//    plain GEMM with fewer such tiles than half the GPU's workgroup slots
+//    also splits K across workgroups (measured on M = 16/32, N = 8192,
+//    K = 8192 with B out of HBM: 36.5 -> 26 us);
+//  * M <= 1024: 128 x 128 tiles, 4 waves of 64 x 64 per K half, the K range
+//    split over two wave groups (more loads in flight per tile);
+//  * larger M: 256 x 256 tiles, 4 waves of 128 x 128 -- MFMA bound.
+template <int FMT>
+hipError_t launch_gemm_t(const GemmProblem& g, hipStream_t s) {
+    const bool plain = g.experts == 0;
+    const int64_t rows_per_problem = plain ? g.M : (g.M + g.experts - 1) / g.experts;
+    if (rows_per_problem <= 64) {
+        const int sp = plain ? choose_splits(tiles_of(g.M, g.N, 32, 64), g.K, 2) : 1;
+        if (sp > 1) return launch_cfg_splitk<FMT, 32, 64, 1, 2, 2, 4, 8>(g, s, sp);
+        return launch_cfg<FMT, 32, 64, 1, 2, 2, 4, 8>(g, s);
+    }
+    if (rows_per_problem <= 1024) return launch_cfg<FMT, 128, 128, 2, 2, 2, 4, 8>(g, s);
+    return launch_cfg<FMT, 256, 256, 2, 2, 1, 4, 8>(g, s);
+}
+
+}  // namespace fp8k

@@ -62,8 +62,12 @@ enum Mode : int {
     MODE_BLOCK = 2,  // as MODE_EXACT, with a scale pair per 32x32 block and 32-deep K block
 };
 
-template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, bool BF16, int MODE, bool SPLITK = false>
+// FMT: operand formats, bit 0 set = A holds E5M2 codes, bit 1 = B (else E4M3).
+template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, bool BF16, int MODE, bool SPLITK = false,
+          int FMT = 0>
 __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
+    static_assert(MODE != MODE_BLOCK || FMT == 0, "the block-scaled form takes E4M3 operands");
+    constexpr int FA = FMT & 1, FB = (FMT >> 1) & 1;
     using C = PipeCfg<BM, BN, WM, WN, KS, NB>;
     constexpr int TM = C::TM, TN = C::TN;
     constexpr bool WIDEN = MODE != MODE_FAST;
@@ -163,9 +167,10 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     auto convert = [&](auto c_c, const Frags<TM, TN>& f) {
         constexpr int c = decltype(c_c)::value;
 #pragma unroll
-        for (int mi = 0; mi < TM; ++mi) ab[c & 1][mi] = e4m3x8_to_bf16(f.a[mi][c / 2][(c % 2) * 2], f.a[mi][c / 2][(c % 2) * 2 + 1]);
+        for (int mi = 0; mi < TM; ++mi)
+            ab[c & 1][mi] = fp8x8_to_bf16<FA>(f.a[mi][c / 2][(c % 2) * 2], f.a[mi][c / 2][(c % 2) * 2 + 1]);
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni) bb[c & 1][ni] = e4m3x8_to_bf16(f.b[ni][c][0], f.b[ni][c][1]);
+        for (int ni = 0; ni < TN; ++ni) bb[c & 1][ni] = fp8x8_to_bf16<FB>(f.b[ni][c][0], f.b[ni][c][1]);
     };
     // MODE_BLOCK: the 32-deep K block's partial product per accumulator block
     // (pieces 2kb and 2kb+1 of the slice), folded into acc with its scale.
@@ -181,7 +186,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
             part[mi][ni] = mfma_32x32x16_bf16(bb[c & 1][ni], ab[c & 1][mi], (c % 2 == 0) ? zero : part[mi][ni]);
         } else {
             constexpr int mi = m / TN, ni = m % TN;
-            acc[mi][ni] = mfma_32x32x64_e4m3(b_op(f, ni), a_op(f, mi), acc[mi][ni]);
+            acc[mi][ni] = mfma_32x32x64_f8<FB, FA>(b_op(f, ni), a_op(f, mi), acc[mi][ni]);
         }
     };
     // MODE_BLOCK scale indices: tile-scale row of each A block and column of
@@ -433,10 +438,11 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     using Store = TileStore<BF16, TM, TN>;
     lds_u8* scratch = lds + (KS > 1 ? C::RED : 0) + (wm * WN + wn) * Store::LDS_BYTES;
     const float scale = MODE == MODE_BLOCK ? 1.0f : p.scale_a[t.expert] * p.scale_b[t.expert];
-    Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch);
+    Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch,
+               p.out_f16 != 0);
 }
 
-template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, int MODE, bool SPLITK = false>
+template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, int MODE, bool SPLITK = false, int FMT = 0>
 hipError_t launch_mode(const GemmProblem& g, hipStream_t s, int32_t splits = 1, float* ws = nullptr,
                        uint32_t* counters = nullptr) {
     GemmArgs a;
@@ -455,14 +461,15 @@ hipError_t launch_mode(const GemmProblem& g, hipStream_t s, int32_t splits = 1, 
     a.tiles_m = g.experts == 0 ? (int32_t)((g.M + BM - 1) / BM)
                                : (int32_t)((g.M + (int64_t)g.experts * (BM - 1)) / BM);
     a.splits = SPLITK ? splits : 1;
+    a.out_f16 = g.out_f16;
     a.ws = ws;
     a.counters = counters;
     const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * a.splits;
     if (blocks == 0) return hipSuccess;
     constexpr int NT = 64 * WM * WN * KS;
     const dim3 grid((unsigned)blocks), block(NT);
-    if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NB, GROUP_M, true, MODE, SPLITK>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NB, GROUP_M, false, MODE, SPLITK>), grid, block, 0, s, a);
+    if (g.out_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NB, GROUP_M, true, MODE, SPLITK, FMT>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KS, NB, GROUP_M, false, MODE, SPLITK, FMT>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 

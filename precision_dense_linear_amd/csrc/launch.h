@@ -8,13 +8,15 @@
 
 namespace fp8k {
 
-hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, hipStream_t s);
+// fmt: 0 = E4M3, 1 = E5M2
+hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, int fmt,
+                                     hipStream_t s);
 hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* tile_scales,
                                    hipStream_t s);
 hipError_t launch_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
-                                   uint8_t* q, float* scales, float* amax, hipStream_t s);
+                                   uint8_t* q, float* scales, float* amax, int fmt, hipStream_t s);
 
-// Dense GEMM on E4M3 codes; `experts` > 0 selects the grouped (MoE) problem,
+// Dense GEMM on FP8 codes; `experts` > 0 selects the grouped (MoE) problem,
 // where M is the total row count T and B holds `experts` K x N matrices.
 struct GemmProblem {
     const uint8_t* A;
@@ -25,12 +27,21 @@ struct GemmProblem {
     const int32_t* offsets;  // grouped only
     int32_t experts;         // 0 for the plain GEMM
     int64_t M, N, K;
-    int32_t out_bf16;
+    int32_t out_bf16;  // 2-byte output (BF16, or FP16 when out_f16)
     int32_t fast_acc;  // 1: native FP8 MFMA accumulation; 0: exact products (BF16 MFMA)
+    int32_t out_f16;   // 2-byte output is IEEE binary16
+    int32_t fmt;       // operand formats: bit 0 set = A holds E5M2 codes, bit 1 = B (else E4M3)
 };
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
 
+// The four operand-format pairs of launch_gemm, each compiled on its own.
+hipError_t launch_gemm_fmt0(const GemmProblem& p, hipStream_t s);
+hipError_t launch_gemm_fmt1(const GemmProblem& p, hipStream_t s);
+hipError_t launch_gemm_fmt2(const GemmProblem& p, hipStream_t s);
+hipError_t launch_gemm_fmt3(const GemmProblem& p, hipStream_t s);
+
+// out: 0 FP32, 1 BF16, 2 FP16
 hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,
-                                   int64_t M, int64_t N, int64_t K, int32_t out_bf16, hipStream_t s);
+                                   int64_t M, int64_t N, int64_t K, int32_t out, hipStream_t s);
 
 }  // namespace fp8k

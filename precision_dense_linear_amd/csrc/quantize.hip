@@ -1,11 +1,14 @@
-// Input side of the scaled FP8 GEMM: amax reduction and E4M3 quantization.
+// Input side of the scaled FP8 GEMM: amax reduction and E4M3 / E5M2
+// quantization.
 //
 // Per-tensor scaling keeps values inside the E4M3 range +-448 ("Triton FP8
 // GEMM via CUTLASS naming", risk paragraph and the scale_max 448 item of its
 // parameter list); 32x32 block scales follow the parameter paragraph of "FP8
-// GEMM in JAX with Triton for Blackwell".  In every mode:
-//     scale = amax / 448 (IEEE binary32 division, 1 for amax == 0)
-//     code  = E4M3_RNE(clamp(fl32(x / scale), -448, 448))
+// GEMM in JAX with Triton for Blackwell", whose opening section also names
+// the E5M2 format.  In every mode, with FMAX = 448 (E4M3) or 57344 (E5M2,
+// per-tensor and row-group quantization only):
+//     scale = amax / FMAX (IEEE binary32 division, 1 for amax == 0)
+//     code  = RNE(clamp(fl32(x / scale), -FMAX, FMAX))
 // All kernels are HBM-bound streams: 16-byte loads, 16-byte code stores.
 #include "device_utils.h"
 #include "launch.h"
@@ -74,10 +77,11 @@ __global__ void __launch_bounds__(kThreads) amax_kernel(const float* __restrict_
 // reads with ordinary (cache-allocating) loads and this pass walks each
 // workgroup's chunks backwards, so it starts on the lines the first pass
 // touched last, the likeliest to still be in the last-level cache.
+template <int F>
 __global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restrict__ x, int64_t n, int64_t cpb,
                                                             const float* __restrict__ amax, uint8_t* __restrict__ q,
                                                             float* scale_out) {
-    const float s = scale_from_amax(*amax);
+    const float s = scale_from_amax_fmt<F>(*amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
     const int64_t n4 = n >> 2;
     const v4f* x4 = reinterpret_cast<const v4f*>(x);
@@ -96,12 +100,12 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restr
         for (int u = 0; u < PT_U; ++u) {
             const int64_t j = c * CHUNK4 + u * 64 + lane;
             if (j < n4)
-                q4[j] = e4m3x4_sat(__fdiv_rn(v[u].x, s), __fdiv_rn(v[u].y, s), __fdiv_rn(v[u].z, s),
-                                   __fdiv_rn(v[u].w, s));
+                q4[j] = fp8x4_sat<F>(__fdiv_rn(v[u].x, s), __fdiv_rn(v[u].y, s), __fdiv_rn(v[u].z, s),
+                                     __fdiv_rn(v[u].w, s));
         }
     }
     if (blockIdx.x == 0)
-        for (int64_t j = (n4 << 2) + threadIdx.x; j < n; j += blockDim.x) q[j] = e4m3_sat(__fdiv_rn(x[j], s));
+        for (int64_t j = (n4 << 2) + threadIdx.x; j < n; j += blockDim.x) q[j] = fp8_sat<F>(__fdiv_rn(x[j], s));
 }
 
 // 32x32 tiles: one wave per tile.  Load j of lane l covers tile row
@@ -212,6 +216,7 @@ __global__ void __launch_bounds__(kThreads) amax_grouped_kernel(const float* __r
 
 // Grouped quantize: same row partition; each row uses its group's scale.
 // Block 0 also writes the scales.
+template <int F>
 __global__ void __launch_bounds__(kThreads) quantize_grouped_kernel(const float* __restrict__ x, int64_t rows,
                                                                     int64_t cols, const int32_t* __restrict__ off,
                                                                     int groups, int64_t rpb,
@@ -220,7 +225,7 @@ __global__ void __launch_bounds__(kThreads) quantize_grouped_kernel(const float*
     __shared__ int64_t bnd[1025];
     load_bounds(off, groups, rows, bnd);
     if (blockIdx.x == 0)
-        for (int g = threadIdx.x; g < groups; g += blockDim.x) scales[g] = scale_from_amax(amax[g]);
+        for (int g = threadIdx.x; g < groups; g += blockDim.x) scales[g] = scale_from_amax_fmt<F>(amax[g]);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t r0 = (int64_t)blockIdx.x * rpb;
     const int64_t r1 = min(r0 + rpb, rows);
@@ -228,7 +233,7 @@ __global__ void __launch_bounds__(kThreads) quantize_grouped_kernel(const float*
     for (int64_t r = r0 + wave; r < r1; r += kThreads / 64) {
         const int g = find_group(bnd, groups, r);
         if (g < 0) continue;
-        const float s = scale_from_amax(amax[g]);
+        const float s = scale_from_amax_fmt<F>(amax[g]);
         const v4f* src = reinterpret_cast<const v4f*>(x + r * cols);
         uint32_t* dst = reinterpret_cast<uint32_t*>(q + r * cols);
         for (int64_t j0 = lane; j0 < c4; j0 += 64 * GQ_U) {
@@ -242,8 +247,8 @@ __global__ void __launch_bounds__(kThreads) quantize_grouped_kernel(const float*
             for (int u = 0; u < GQ_U; ++u) {
                 const int64_t j = j0 + u * 64;
                 if (j < c4)
-                    dst[j] = e4m3x4_sat(__fdiv_rn(v[u].x, s), __fdiv_rn(v[u].y, s), __fdiv_rn(v[u].z, s),
-                                        __fdiv_rn(v[u].w, s));
+                    dst[j] = fp8x4_sat<F>(__fdiv_rn(v[u].x, s), __fdiv_rn(v[u].y, s), __fdiv_rn(v[u].z, s),
+                                          __fdiv_rn(v[u].w, s));
             }
         }
     }
@@ -251,7 +256,8 @@ __global__ void __launch_bounds__(kThreads) quantize_grouped_kernel(const float*
 
 }  // namespace
 
-hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, hipStream_t s) {
+hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, int fmt,
+                                     hipStream_t s) {
     hipLaunchKernelGGL(fill_f32, dim3(1), dim3(64), 0, s, amax, 1, 0.0f);
     // up to 2048 workgroups of contiguous chunks (at least one workgroup)
     const int64_t nchunks = ((n >> 2) + CHUNK4 - 1) / CHUNK4;
@@ -259,8 +265,12 @@ hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, floa
     const int64_t blocks = nchunks < 1 ? 1 : (nchunks + cpb - 1) / cpb;
     if (n > 0)
         hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, n, cpb, amax);
-    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, n, cpb, (const float*)amax, q,
-                       scale);
+    if (fmt == 0)
+        hipLaunchKernelGGL(quantize_kernel<0>, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, n, cpb,
+                           (const float*)amax, q, scale);
+    else
+        hipLaunchKernelGGL(quantize_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, n, cpb,
+                           (const float*)amax, q, scale);
     return hipGetLastError();
 }
 
@@ -275,7 +285,7 @@ hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, u
 }
 
 hipError_t launch_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
-                                   uint8_t* q, float* scales, float* amax, hipStream_t s) {
+                                   uint8_t* q, float* scales, float* amax, int fmt, hipStream_t s) {
     hipLaunchKernelGGL(fill_f32, dim3((groups + 255) / 256), dim3(256), 0, s, amax, groups, 0.0f);
     // contiguous row runs: up to 2048 workgroups, at least one row each
     const int64_t nblk = rows < 1 ? 1 : (rows < 2048 ? rows : 2048);
@@ -284,8 +294,12 @@ hipError_t launch_quantize_grouped(const float* x, int64_t rows, int64_t cols, c
     if (rows > 0 && cols > 0)
         hipLaunchKernelGGL(amax_grouped_kernel, dim3(blocks), dim3(kThreads), 0, s, x, rows, cols, offsets, groups,
                            rpb, amax);
-    hipLaunchKernelGGL(quantize_grouped_kernel, dim3(blocks), dim3(kThreads), 0, s, x, rows, cols, offsets, groups,
-                       rpb, (const float*)amax, q, scales);
+    if (fmt == 0)
+        hipLaunchKernelGGL(quantize_grouped_kernel<0>, dim3(blocks), dim3(kThreads), 0, s, x, rows, cols, offsets,
+                           groups, rpb, (const float*)amax, q, scales);
+    else
+        hipLaunchKernelGGL(quantize_grouped_kernel<1>, dim3(blocks), dim3(kThreads), 0, s, x, rows, cols, offsets,
+                           groups, rpb, (const float*)amax, q, scales);
     return hipGetLastError();
 }
 

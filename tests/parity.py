@@ -8,6 +8,7 @@
   where an FP32 accumulator cannot resolve the BF16 rounding), an element
   also passes if |C_gpu - C_exact| <= FP32 bound + 1 BF16 ulp; such elements
   are counted and reported separately.
+* FP16 output: the same rule with binary16 ulps.
 """
 from __future__ import annotations
 
@@ -62,9 +63,40 @@ def check_bf16(c_bits: np.ndarray, oracle_bits: np.ndarray, exact: np.ndarray, s
     return int(d[ok].max()) if ok.any() else 0, int(extra.sum())
 
 
+def f16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return bits.astype(np.uint16).view(np.float16).astype(np.float64)
+
+
+def f16_ulp(x: np.ndarray) -> np.ndarray:
+    _, e = np.frexp(np.abs(x))
+    return np.maximum(np.ldexp(1.0, e - 11), 2.0 ** -24)   # 11 significand bits, subnormal step 2^-24
+
+
+def check_f16(c_bits: np.ndarray, oracle_bits: np.ndarray, exact: np.ndarray, sumabs_scaled: np.ndarray,
+              what: str = ""):
+    """The BF16 rule for IEEE binary16 output: within 1 ulp (monotone order of
+    the bit patterns, +-Inf one step past the largest finite value) of the
+    oracle's correctly rounded value, with the same cancellation allowance.
+    Returns (max ulp distance, count passed only under the allowance)."""
+    d = np.abs(bf16_ord(c_bits) - bf16_ord(oracle_bits))   # same sign-magnitude 16-bit ordering
+    ok = d <= 1
+    fbound = REL_F32 * sumabs_scaled
+    cancel = fbound > 0.5 * f16_ulp(exact)
+    with np.errstate(invalid="ignore"):
+        alt = cancel & (np.abs(f16_to_f64(c_bits) - exact) <= fbound + f16_ulp(exact))
+    extra = (~ok) & alt
+    bad = (~ok) & (~alt)
+    if bad.any():
+        i = int(np.argmax(np.where(bad, d, -1)))
+        raise AssertionError("%s: %d of %d FP16 outputs more than 1 ulp from the oracle (worst %d ulp: got %#06x "
+                             "want %#06x, exact %r)" % (what, int(bad.sum()), d.size, int(d.flat[i]),
+                                                        int(c_bits.flat[i]), int(oracle_bits.flat[i]), exact.flat[i]))
+    return int(d[ok].max()) if ok.any() else 0, int(extra.sum())
+
+
 def to_bits(c) -> np.ndarray:
-    """A torch output tensor (float32 or bfloat16) -> numpy bits (uint32 / uint16)."""
+    """A torch output tensor (float32, bfloat16 or float16) -> numpy bits (uint32 / uint16)."""
     import torch
-    if c.dtype == torch.bfloat16:
+    if c.dtype in (torch.bfloat16, torch.float16):
         return c.view(torch.int16).cpu().numpy().view(np.uint16)
     return c.cpu().numpy().view(np.uint32)

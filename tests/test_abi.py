@@ -26,8 +26,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fp8_quantize", "fp8_quantize_blocked", "fp8_quantize_grouped", "fp8_gemm",
-              "fp8_gemm_blockscaled", "fp8_grouped_gemm", "fp8_status_string", "fp8_last_error"):
+    for n in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_grouped",
+              "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
+              "fp8_status_string", "fp8_last_error"):
         assert n in names
 
 
@@ -59,6 +60,9 @@ def gemm(A=FAKE, B=FAKE, sa=FAKE, sb=FAKE, C=FAKE, M=64, N=64, K=64, out=1):
     (dict(M=-1), P.FP8_ERR_INVALID_ARG),
     (dict(K=-16), P.FP8_ERR_INVALID_ARG),
     (dict(out=7), P.FP8_ERR_INVALID_ARG),
+    (dict(out=3), P.FP8_ERR_INVALID_ARG),
+    (dict(out=1 | 0x800), P.FP8_ERR_INVALID_ARG),             # unknown flag bit
+    (dict(out=2 | 0x200 | 0x400 | 0x100, M=0), P.FP8_OK),     # FP16 out, both E5M2, fast: accepted
     (dict(A=FAKE_ODD), P.FP8_ERR_INVALID_ARG),
     (dict(K=40), P.FP8_ERR_UNSUPPORTED_SHAPE),
     (dict(N=40), P.FP8_ERR_UNSUPPORTED_SHAPE),
@@ -78,6 +82,9 @@ def test_blockscaled_validation():
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 48, 1, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
     assert f(FAKE, FAKE, None, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 1, None) == P.FP8_OK
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 2, None) == P.FP8_OK                 # FP16 out
+    for flag in (P.FP8_A_E5M2, P.FP8_B_E5M2, P.FP8_ACC_FAST):                              # E4M3, exact only
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 1 | flag, None) == P.FP8_ERR_INVALID_ARG
 
 
 def test_grouped_validation():
@@ -95,6 +102,10 @@ def test_quantize_validation():
     assert L.fp8_quantize(FAKE, -1, FAKE, FAKE, FAKE, None) == P.FP8_ERR_INVALID_ARG
     assert L.fp8_quantize(FAKE_ODD, 16, FAKE, FAKE, ctypes.c_void_p(0x200000), None) == P.FP8_ERR_INVALID_ARG
     assert L.fp8_quantize(FAKE, 16, FAKE, FAKE, FAKE, None) == P.FP8_ERR_INVALID_ARG   # scale aliases amax
+    assert L.fp8_quantize_e5m2(None, 16, FAKE, FAKE, FAKE, None) == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize_e5m2(FAKE, 16, FAKE, FAKE, FAKE, None) == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize_grouped_e5m2(FAKE, 64, 64, FAKE, 0, FAKE, FAKE, ctypes.c_void_p(0x200000), None) \
+        == P.FP8_ERR_INVALID_ARG
     assert L.fp8_quantize_blocked(FAKE, 48, 64, FAKE, FAKE, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
     assert L.fp8_quantize_blocked(FAKE, 64, 64, None, FAKE, None) == P.FP8_ERR_INVALID_ARG
     assert L.fp8_quantize_grouped(FAKE, 64, 64, FAKE, 0, FAKE, FAKE, ctypes.c_void_p(0x200000), None) \
@@ -107,3 +118,11 @@ def test_binding_refuses_wrong_operand_dtype():
     import torch
     with pytest.raises(TypeError):
         P._codes(torch.zeros(4, dtype=torch.float16))
+    # a float8_e5m2 tensor cannot be passed as E4M3 codes, and the format must be known
+    with pytest.raises(ValueError):
+        P._fmt_flag(torch.zeros(4, dtype=torch.float8_e5m2), "e4m3", P.FP8_A_E5M2)
+    with pytest.raises(ValueError):
+        P._fmt_flag(torch.zeros(4, dtype=torch.uint8), "e3m4", P.FP8_A_E5M2)
+    assert P._fmt_flag(torch.zeros(4, dtype=torch.float8_e5m2), None, P.FP8_B_E5M2) == P.FP8_B_E5M2
+    assert P._fmt_flag(torch.zeros(4, dtype=torch.uint8), "e5m2", P.FP8_A_E5M2) == P.FP8_A_E5M2
+    assert P._fmt_flag(torch.zeros(4, dtype=torch.uint8), None, P.FP8_A_E5M2) == 0

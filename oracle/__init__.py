@@ -19,6 +19,9 @@ paragraph -- grouped GEMM over experts):
 * ``gemm_blockscaled_rows`` -- per-32-K-block exact partials, scaled by
                           s_a*s_b and summed in FP64, rounded once.
 * ``grouped_gemm_rows`` -- the per-tensor GEMM applied per expert group.
+* ``quantize_blocked_t`` / ``gemm_blockscaled_rows_t`` -- block scales of
+                          32x32 or 64x64 tiles (the Blackwell page's
+                          granularity and its coarser fallback).
 * ``e5m2_table``, ``quantize_*_fmt``, ``gemm_rows_fmt`` -- the same for OCP
                           E5M2 operands (scale = fl32(amax/57344)) and mixed
                           E4M3 x E5M2 pairs, summed exactly in 128-bit
@@ -101,6 +104,8 @@ def lib():
         L.orc_gemm_rows_fmt.restype = ctypes.c_int
         L.orc_gemm_rows_fmt.argtypes = [P, P, ctypes.c_int, ctypes.c_int, f32, f32, i64, i64, P, i64, ctypes.c_int,
                                         P, P, P]
+        L.orc_quantize_blocked_t.argtypes = [P, i64, i64, ctypes.c_int, P, P]
+        L.orc_gemm_blockscaled_rows_t.argtypes = [P, P, P, P, i64, i64, ctypes.c_int, P, i64, ctypes.c_int, P, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -411,4 +416,42 @@ def gemm_rows_fmt(qa, qb, fa, fb, sa, sb, kind, rows=None):
                                  nr, kind, _p(out), _p(exact), _p(sab))
     if st != 0:
         raise OverflowError("sum too large for the oracle's 128-bit scaled product")
+    return (out if kind == F32 else out.astype(np.uint16)), exact, sab
+
+
+# --------------------------------------------------------------------------
+# Block-scale granularity T = 32 or 64 ("FP8 GEMM in JAX with Triton for
+# Blackwell": 32x32 blocks in the parameter paragraph, 64x64 as the coarser
+# granularity of the monitoring paragraph)
+# --------------------------------------------------------------------------
+def quantize_blocked_t(x: np.ndarray, T: int):
+    """T x T tiles; returns (codes, tile scales float32[rows/T, cols/T])."""
+    x = _c(x, np.float32)
+    rows, cols = x.shape
+    assert rows % T == 0 and cols % T == 0
+    q = np.empty(x.shape, dtype=np.uint8)
+    ts = np.empty((rows // T, cols // T), dtype=np.float32)
+    lib().orc_quantize_blocked_t(_p(x), rows, cols, T, _p(q), _p(ts))
+    return q, ts
+
+
+def gemm_blockscaled_rows_t(qa, qb, s_a, s_b, T, kind, rows=None):
+    """Block-scaled GEMM with T-deep K blocks and T x T scale tiles on the
+    selected rows: (bits uint32 (FP32) / uint16 (BF16, FP16), FP64 sum,
+    scaled sumabs)."""
+    qa = _c(qa, np.uint8)
+    qb = _c(qb, np.uint8)
+    s_a = _c(s_a, np.float32)
+    s_b = _c(s_b, np.float32)
+    M, K = qa.shape
+    N = qb.shape[1]
+    assert M % T == 0 and N % T == 0 and K % T == 0
+    assert s_a.shape == (M // T, K // T) and s_b.shape == (K // T, N // T)
+    rows = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    nr = rows.size
+    out = np.empty((nr, N), np.uint32)
+    exact = np.empty((nr, N), np.float64)
+    sab = np.empty((nr, N), np.float64)
+    lib().orc_gemm_blockscaled_rows_t(_p(qa), _p(qb), _p(s_a), _p(s_b), N, K, T, _p(rows), nr, kind, _p(out),
+                                      _p(exact), _p(sab))
     return (out if kind == F32 else out.astype(np.uint16)), exact, sab

@@ -644,3 +644,84 @@ int orc_gemm_rows_fmt(const uint8_t* A, const uint8_t* B, int fa, int fb, float 
     }
     return status;
 }
+
+/* ======================================================================== */
+/* Block-scale granularity as a parameter.  "FP8 GEMM in JAX with Triton for  */
+/* Blackwell": the parameter paragraph sets the scale granularity to 32x32    */
+/* blocks; its monitoring paragraph names 64x64 as the coarser granularity to */
+/* move to when accuracy suffers.  Both are T x T tiles of A (rows x K) and   */
+/* of B (K x columns), T = 32 or 64, each quantized with its own              */
+/* fl32(tile_amax / 448).                                                      */
+/* ======================================================================== */
+
+/* T x T tile quantization (rows, cols multiples of T); scales row-major as
+ * [rows/T][cols/T]. */
+void orc_quantize_blocked_t(const float* x, int64_t rows, int64_t cols, int T, uint8_t* q, float* tile_scales) {
+    int64_t tr = rows / T, tc = cols / T;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < tr * tc; t++) {
+        int64_t bi = t / tc, bj = t % tc;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < T; i++)
+            for (int64_t j = 0; j < T; j++) {
+                float a = fabsf(x[(bi * T + i) * cols + bj * T + j]);
+                if (a > amax) amax = a;
+            }
+        float s = orc_scale_from_amax(amax);
+        tile_scales[t] = s;
+        for (int64_t i = 0; i < T; i++)
+            for (int64_t j = 0; j < T; j++) {
+                int64_t idx = (bi * T + i) * cols + bj * T + j;
+                volatile float quot = x[idx] / s;
+                q[idx] = orc_e4m3_rne_sat(quot);
+            }
+    }
+}
+
+/* Block-scaled GEMM with T-deep K blocks and T x T scale tiles:
+ *   P_kb[i,j] = sum_{k in [T*kb, T*kb + T)} a[i,k]*b[k,j]          (exact)
+ *   C[i,j]    = sum_kb s_a[i/T, kb] * s_b[kb, j/T] * P_kb[i,j]     (FP64)
+ * rounded once to FP32 / BF16 / FP16 (kind 0 / 1 / 2; one uint32 of bits per
+ * output).  exact receives the FP64 sum, sabs sum_kb s_a*s_b*sum_k |a*b|. */
+void orc_gemm_blockscaled_rows_t(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b,
+                                 int64_t N, int64_t K, int T, const int64_t* rows, int64_t nr, int kind,
+                                 uint32_t* out, double* exact, double* sabs) {
+    double tab[256];
+    orc_e4m3_table(tab);
+    for (int c = 0; c < 256; c++) if (isnan(tab[c])) tab[c] = 0.0;
+    int64_t KB = K / T, NBT = N / T;
+#pragma omp parallel
+    {
+        double* part = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double* apart = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nr; r++) {
+            int64_t i = rows[r];
+            double* crow = exact + r * N;
+            double* srow = sabs + r * N;
+            for (int64_t j = 0; j < N; j++) { crow[j] = 0.0; srow[j] = 0.0; }
+            for (int64_t kb = 0; kb < KB; kb++) {
+                for (int64_t j = 0; j < N; j++) { part[j] = 0.0; apart[j] = 0.0; }
+                for (int64_t k = kb * T; k < kb * T + T; k++) {
+                    double a = tab[A[i * K + k]];
+                    if (a == 0.0) continue;
+                    const uint8_t* brow = B + k * N;
+                    for (int64_t j = 0; j < N; j++) {
+                        double p = a * tab[brow[j]];
+                        part[j] += p;
+                        apart[j] += fabs(p);
+                    }
+                }
+                double sa = (double)s_a[(i / T) * KB + kb];
+                for (int64_t j = 0; j < N; j++) {
+                    double sab = sa * (double)s_b[kb * NBT + j / T];
+                    crow[j] += sab * part[j];
+                    srow[j] += sab * apart[j];
+                }
+            }
+            for (int64_t j = 0; j < N; j++) out[r * N + j] = orc_round_ieee_f64(crow[j], kind);
+        }
+        free(part);
+        free(apart);
+    }
+}

@@ -114,7 +114,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gemm8192",
                     choices=["gemm8192", "gemm1024", "gemm256", "llm16", "llm128", "llm4096", "blockscaled8192",
-                             "moe", "mixed8192"])
+                             "moe", "mixed8192", "blockscaled8192_64"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy twice (reference for the HBM byte counters)")
@@ -158,11 +158,13 @@ class Workload:
             a, b = W.llm_linear(self.M, self.N, self.K)
             self.desc = ("LLM linear layer M=%d N=%d K=%d, per-tensor FP8, BF16 out; activations N(0,1) with 1%% "
                          "outlier channels x20, weights N(0,0.02)" % (self.M, self.N, self.K))
-        elif name == "blockscaled8192":
+        elif name.startswith("blockscaled8192"):
             self.kind = "block"
+            self.block = 64 if name.endswith("_64") else 32
             self.M = self.N = self.K = 8192
-            a, b = W.blockscaled_pair(8192, 8192, 8192)
-            self.desc = "block-scaled (32x32 tiles) FP8 GEMM M=N=K=8192, BF16 out; tile factors 10^U(-2,2)"
+            a, b = W.blockscaled_pair(8192, 8192, 8192, tile=self.block)
+            self.desc = ("block-scaled (%dx%d tiles) FP8 GEMM M=N=K=8192, BF16 out; tile factors 10^U(-2,2)"
+                         % (self.block, self.block))
         else:
             self.kind = "moe"
             x, w, off = W.moe()
@@ -182,8 +184,8 @@ class Workload:
             self.sa, self.aa = (torch.empty(1, device=dev) for _ in range(2))
             self.sb, self.ab = (torch.empty(1, device=dev) for _ in range(2))
         elif self.kind == "block":
-            self.sa = torch.empty((self.M // 32, self.K // 32), device=dev)
-            self.sb = torch.empty((self.K // 32, self.N // 32), device=dev)
+            self.sa = torch.empty((self.M // self.block, self.K // self.block), device=dev)
+            self.sb = torch.empty((self.K // self.block, self.N // self.block), device=dev)
         else:
             self.sa, self.aa = (torch.empty(self.E, device=dev) for _ in range(2))
             self.sb, self.ab = (torch.empty(self.E, device=dev) for _ in range(2))
@@ -195,8 +197,9 @@ class Workload:
             P.fp8_quantize(self.A, self.qa, self.sa, self.aa)
             (P.fp8_quantize_e5m2 if self.b_e5m2 else P.fp8_quantize)(self.B, self.qb, self.sb, self.ab)
         elif self.kind == "block":
-            P.fp8_quantize_blocked(self.A, self.qa, self.sa)
-            P.fp8_quantize_blocked(self.B, self.qb, self.sb)
+            qb = P.fp8_quantize_blocked64 if self.block == 64 else P.fp8_quantize_blocked
+            qb(self.A, self.qa, self.sa)
+            qb(self.B, self.qb, self.sb)
         else:
             P.fp8_quantize_grouped(self.A, self.off, self.qa, self.sa, self.aa)
             P.fp8_quantize_grouped(self.B, self.woff, self.qb, self.sb, self.ab)
@@ -209,7 +212,7 @@ class Workload:
             P.fp8_gemm(qa, qb, self.sa, self.sb, self.out, C=self.C, fast=fast,
                        b_fmt="e5m2" if self.b_e5m2 else "e4m3")
         elif self.kind == "block":
-            P.fp8_gemm_blockscaled(qa, qb, self.sa, self.sb, self.out, C=self.C)
+            P.fp8_gemm_blockscaled(qa, qb, self.sa, self.sb, self.out, C=self.C, block=self.block)
         else:
             P.fp8_grouped_gemm(qa, qb.view(self.E, self.K, self.N), self.off, self.sa, self.sb, self.out,
                                C=self.C, fast=fast)
@@ -223,7 +226,8 @@ class Workload:
         osz = 4 if self.out == self.torch.float32 else 2
         if self.kind == "moe":
             return self.M * self.K + self.E * self.K * self.N + self.M * self.N * osz
-        extra = (self.M // 32) * (self.K // 32) * 4 + (self.K // 32) * (self.N // 32) * 4 if self.kind == "block" else 0
+        t = getattr(self, "block", 32)
+        extra = (self.M // t) * (self.K // t) * 4 + (self.K // t) * (self.N // t) * 4 if self.kind == "block" else 0
         return self.M * self.K + self.K * self.N + self.M * self.N * osz + extra
 
 
@@ -375,7 +379,8 @@ def main():
                 "basis": rotation,
                 "in_step_avg_kernel_us": round(avg_gemm_ms * 1e3, 2)}
     roof["kernel"] = "gemm_kernel (fp8_gemm)" if w.kind == "pertensor" else (
-        "gemm_kernel MODE_BLOCK (fp8_gemm_blockscaled)" if w.kind == "block" else "gemm_kernel (fp8_grouped_gemm)")
+        ("gemm_kernel MODE_BLOCK64 (fp8_gemm_blockscaled, 64x64 tiles)" if getattr(w, "block", 32) == 64 else
+         "gemm_kernel MODE_BLOCK (fp8_gemm_blockscaled)") if w.kind == "block" else "gemm_kernel (fp8_grouped_gemm)")
     roof["avg_kernel_us"] = round((avg_gemm_ms if mfma_bound else hbm_ms) * 1e3, 2)
     mhz = sclk.mean_mhz()
     sclk_out = None

@@ -101,6 +101,14 @@ typedef enum fp8_out_dtype {
 #define FP8_B_E5M2 0x400
 
 /*
+ * Scale-tile edge of fp8_gemm_blockscaled, OR-ed into its out_dtype: 64x64
+ * tiles and 64-deep K blocks instead of 32x32 ([P3] monitoring paragraph:
+ * the coarser 64x64 granularity to move to when accuracy suffers).  Not
+ * accepted by the other GEMMs.
+ */
+#define FP8_BLOCK64 0x800
+
+/*
  * Per-tensor quantization ([P1] risk paragraph: per-tensor scaling keeps
  * values within the E4M3 range +-448; parameter list: scale_max 448):
  *     amax  = max_i |x_i|
@@ -135,6 +143,16 @@ fp8_status fp8_quantize_e5m2(const float* x, int64_t n, uint8_t* q, float* scale
  */
 fp8_status fp8_quantize_blocked(const float* x, int64_t rows, int64_t cols, uint8_t* q,
                                 float* tile_scales, void* stream);
+
+/*
+ * 64x64-tile quantization ([P3] monitoring paragraph: 64x64 as the coarser
+ * scale granularity): fp8_quantize_blocked with 64x64 tiles; tile (bi, bj)
+ * covers rows 64bi..64bi+63 and columns 64bj..64bj+63, its scale is stored at
+ * tile_scales[bi * (cols/64) + bj].  rows, cols >= 0 and multiples of 64
+ * (else FP8_ERR_UNSUPPORTED_SHAPE); x, q 16-byte aligned.
+ */
+fp8_status fp8_quantize_blocked64(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* tile_scales,
+                                  void* stream);
 
 /*
  * Row-group quantization, one scale per group ([P3] MoE paragraph with the
@@ -191,6 +209,9 @@ fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, co
  * accumulated in FP32; each block's partial products are exact (default
  * accumulation mode; FP8_ACC_FAST and the operand-format flags are not
  * accepted here: E4M3 operands only).  C is FP32, BF16 or FP16.
+ * With FP8_BLOCK64 in out_dtype the blocks are 64 deep and the scale tiles
+ * 64x64: s_a (M/64) x (K/64), s_b (K/64) x (N/64) (as written by
+ * fp8_quantize_blocked64), and M, N, K must be multiples of 64.
  * s_a: (M/32) x (K/32) floats, s_b: (K/32) x (N/32)
  * floats, row-major, on the device (as written by fp8_quantize_blocked).
  * M, N, K >= 0 and multiples of 32, K <= 2^23, else

@@ -10,10 +10,11 @@ Entry points (same names as the C ABI):
     fp8_quantize(x)                          -> (q, scale, amax)
     fp8_quantize_e5m2(x)                     -> (q, scale, amax)
     fp8_quantize_blocked(x)                  -> (q, tile_scales)
+    fp8_quantize_blocked64(x)                -> (q, tile_scales)
     fp8_quantize_grouped(x, offsets)         -> (q, scales, amax)
     fp8_quantize_grouped_e5m2(x, offsets)    -> (q, scales, amax)
     fp8_gemm(A, B, scale_a, scale_b, out_dtype)
-    fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype)
+    fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype, block=32 | 64)
     fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype)
 FP8 codes are passed as torch.uint8 (E4M3 unless a_fmt / b_fmt say "e5m2"),
 torch.float8_e4m3fn or torch.float8_e5m2 tensors; out_dtype is
@@ -33,8 +34,10 @@ FP8_OK, FP8_ERR_INVALID_ARG, FP8_ERR_UNSUPPORTED_SHAPE, FP8_ERR_HIP = 0, 1, 2, 3
 FP8_OUT_F32, FP8_OUT_BF16, FP8_OUT_F16 = 0, 1, 2
 FP8_ACC_FAST = 0x100  # native FP8 matrix-core accumulation (see include/fp8gemm.h)
 FP8_A_E5M2, FP8_B_E5M2 = 0x200, 0x400  # operand formats (default E4M3)
+FP8_BLOCK64 = 0x800  # 64x64 scale tiles for the block-scaled GEMM
 
-SYMBOLS = ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_grouped",
+SYMBOLS = ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
+           "fp8_quantize_grouped",
            "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
            "fp8_status_string", "fp8_last_error")
 
@@ -55,12 +58,14 @@ def _load():
     L.fp8_quantize.argtypes = [P, i64, P, P, P, P]
     L.fp8_quantize_e5m2.argtypes = [P, i64, P, P, P, P]
     L.fp8_quantize_blocked.argtypes = [P, i64, i64, P, P, P]
+    L.fp8_quantize_blocked64.argtypes = [P, i64, i64, P, P, P]
     L.fp8_quantize_grouped.argtypes = [P, i64, i64, P, i32, P, P, P, P]
     L.fp8_quantize_grouped_e5m2.argtypes = [P, i64, i64, P, i32, P, P, P, P]
     L.fp8_gemm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_gemm_blockscaled.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i64, i64, i64, i32, P]
-    for f in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_grouped",
+    for f in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
+              "fp8_quantize_grouped",
               "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
         getattr(L, f).restype = st
     L.fp8_status_string.restype = ctypes.c_char_p
@@ -147,19 +152,27 @@ def fp8_quantize_e5m2(x: torch.Tensor, q=None, scale=None, amax=None, stream=Non
     return _quantize("fp8_quantize_e5m2", x, q, scale, amax, stream)
 
 
-def fp8_quantize_blocked(x: torch.Tensor, q=None, tile_scales=None, stream=None):
-    """32x32-tile E4M3 quantization of a 2-D tensor; returns (q, tile_scales[rows/32, cols/32])."""
+def _quantize_blocked(func: str, T: int, x, q, tile_scales, stream):
     _require(x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 2,
              "x must be a contiguous 2-D float32 GPU tensor")
     rows, cols = x.shape
     dev = x.device
     q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else q
     if tile_scales is None:
-        tile_scales = torch.empty((rows // 32, cols // 32), dtype=torch.float32, device=dev)
+        tile_scales = torch.empty((rows // T, cols // T), dtype=torch.float32, device=dev)
     with torch.cuda.device(dev):
-        _check("fp8_quantize_blocked", lib.fp8_quantize_blocked(_ptr(x), rows, cols, _ptr(q), _ptr(tile_scales),
-                                                                _stream(dev, stream)))
+        _check(func, getattr(lib, func)(_ptr(x), rows, cols, _ptr(q), _ptr(tile_scales), _stream(dev, stream)))
     return q, tile_scales
+
+
+def fp8_quantize_blocked(x: torch.Tensor, q=None, tile_scales=None, stream=None):
+    """32x32-tile E4M3 quantization of a 2-D tensor; returns (q, tile_scales[rows/32, cols/32])."""
+    return _quantize_blocked("fp8_quantize_blocked", 32, x, q, tile_scales, stream)
+
+
+def fp8_quantize_blocked64(x: torch.Tensor, q=None, tile_scales=None, stream=None):
+    """64x64-tile E4M3 quantization of a 2-D tensor; returns (q, tile_scales[rows/64, cols/64])."""
+    return _quantize_blocked("fp8_quantize_blocked64", 64, x, q, tile_scales, stream)
 
 
 def _quantize_grouped(func: str, x, offsets, q, scales, amax, stream):
@@ -214,8 +227,10 @@ def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=No
     return C
 
 
-def fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype=torch.bfloat16, C=None, stream=None):
-    """C = sum over 32-wide K blocks of s_a*s_b * (A_kb @ B_kb), 32x32 tile scales (E4M3 operands)."""
+def fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype=torch.bfloat16, C=None, stream=None, block=32):
+    """C = sum over block-deep K blocks of s_a*s_b * (A_kb @ B_kb), block x block tile scales
+    (block 32 or 64; E4M3 operands)."""
+    _require(block in (32, 64), "block must be 32 or 64")
     _require(_fmt_flag(A, None, 1) == 0 and _fmt_flag(B, None, 1) == 0, "the block-scaled GEMM takes E4M3 operands")
     A, B = _codes(A), _codes(B)
     M, K = A.shape
@@ -225,7 +240,8 @@ def fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype=torch.bfloat16, C=None, strea
     C = _out_tensor(C, (M, N), code, A.device)
     with torch.cuda.device(A.device):
         _check("fp8_gemm_blockscaled", lib.fp8_gemm_blockscaled(_ptr(A), _ptr(B), _ptr(s_a), _ptr(s_b), _ptr(C),
-                                                                M, N, K, code, _stream(A.device, stream)))
+                                                                M, N, K, code | (FP8_BLOCK64 if block == 64 else 0),
+                                                                _stream(A.device, stream)))
     return C
 
 

@@ -36,15 +36,16 @@ constexpr int64_t kMaxK = int64_t(1) << 23;  // 256 rows x K stays below 2^31 by
 constexpr int64_t kMaxN = int64_t(1) << 20;  // 256 K-rows x N stays below 2^31 bytes per step
 
 fp8_status check_gemm_common(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
-                             int32_t out_dtype) {
+                             int32_t out_dtype, int32_t allowed_flags) {
     if (M < 0 || N < 0 || K < 0) return fail(FP8_ERR_INVALID_ARG, "negative size (M=%lld N=%lld K=%lld)",
                                              (long long)M, (long long)N, (long long)K);
     // an operand with no elements may be null
     if ((!A && M * K > 0) || (!B && K * N > 0) || (!C && M * N > 0))
         return fail(FP8_ERR_INVALID_ARG, "null matrix pointer");
     const int32_t base = out_dtype & 0xFF;
-    if (out_dtype & ~(0xFF | FP8_ACC_FAST | FP8_A_E5M2 | FP8_B_E5M2))
-        return fail(FP8_ERR_INVALID_ARG, "out_dtype %#x has unknown flag bits", out_dtype);
+    if (out_dtype & ~(0xFF | allowed_flags))
+        return fail(FP8_ERR_INVALID_ARG, "out_dtype %#x has flag bits this call does not take (%#x)", out_dtype,
+                    out_dtype & ~(0xFF | allowed_flags));
     if (base != FP8_OUT_F32 && base != FP8_OUT_BF16 && base != FP8_OUT_F16)
         return fail(FP8_ERR_INVALID_ARG,
                     "out_dtype %#x is not FP8_OUT_F32, FP8_OUT_BF16 or FP8_OUT_F16 (| FP8_ACC_FAST, FP8_A_E5M2, "
@@ -73,6 +74,18 @@ fp8_status quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scal
     if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
     if (scale == amax) return fail(FP8_ERR_INVALID_ARG, "scale and amax must be distinct");
     return from_hip(fp8k::launch_quantize_pertensor(x, n, q, scale, amax, fmt, (hipStream_t)stream), what);
+}
+
+fp8_status quantize_blocked(const float* x, int64_t rows, int64_t cols, int T, uint8_t* q, float* tile_scales,
+                            void* stream, const char* what) {
+    if (!x || !q || !tile_scales) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
+    if (rows < 0 || cols < 0) return fail(FP8_ERR_INVALID_ARG, "negative size");
+    if (rows % T || cols % T)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "rows=%lld and cols=%lld must be multiples of %d", (long long)rows,
+                    (long long)cols, T);
+    if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
+    if ((rows / T) * (cols / T) > (int64_t(1) << 34)) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "too many tiles");
+    return from_hip(fp8k::launch_quantize_blocked(x, rows, cols, T, q, tile_scales, (hipStream_t)stream), what);
 }
 
 fp8_status quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
@@ -115,16 +128,12 @@ fp8_status fp8_quantize_e5m2(const float* x, int64_t n, uint8_t* q, float* scale
 
 fp8_status fp8_quantize_blocked(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* tile_scales,
                                 void* stream) {
-    if (!x || !q || !tile_scales) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
-    if (rows < 0 || cols < 0) return fail(FP8_ERR_INVALID_ARG, "negative size");
-    if (rows % 32 || cols % 32)
-        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "rows=%lld and cols=%lld must be multiples of 32", (long long)rows,
-                    (long long)cols);
-    if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
-    if ((rows / 32) * (cols / 32) > (int64_t(1) << 34))
-        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "too many tiles");
-    return from_hip(fp8k::launch_quantize_blocked(x, rows, cols, q, tile_scales, (hipStream_t)stream),
-                    "fp8_quantize_blocked");
+    return quantize_blocked(x, rows, cols, 32, q, tile_scales, stream, "fp8_quantize_blocked");
+}
+
+fp8_status fp8_quantize_blocked64(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* tile_scales,
+                                  void* stream) {
+    return quantize_blocked(x, rows, cols, 64, q, tile_scales, stream, "fp8_quantize_blocked64");
 }
 
 fp8_status fp8_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
@@ -139,7 +148,7 @@ fp8_status fp8_quantize_grouped_e5m2(const float* x, int64_t rows, int64_t cols,
 
 fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
                     int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
-    fp8_status st = check_gemm_common(A, B, C, M, N, K, out_dtype);
+    fp8_status st = check_gemm_common(A, B, C, M, N, K, out_dtype, FP8_ACC_FAST | FP8_A_E5M2 | FP8_B_E5M2);
     if (st != FP8_OK) return st;
     if (!scale_a || !scale_b) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
     if (K % 16 || N % 16)
@@ -152,25 +161,26 @@ fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, co
 
 fp8_status fp8_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,
                                 int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
-    fp8_status st = check_gemm_common(A, B, C, M, N, K, out_dtype);
-    if (st != FP8_OK) return st;
-    if (!s_a || !s_b) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
     if (out_dtype & FP8_ACC_FAST)
         return fail(FP8_ERR_INVALID_ARG, "FP8_ACC_FAST is not available for the block-scaled GEMM");
     if (out_dtype & (FP8_A_E5M2 | FP8_B_E5M2))
         return fail(FP8_ERR_INVALID_ARG, "the block-scaled GEMM takes E4M3 operands only");
-    if (M % 32 || N % 32 || K % 32)
-        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "M=%lld N=%lld K=%lld must be multiples of 32", (long long)M,
-                    (long long)N, (long long)K);
+    fp8_status st = check_gemm_common(A, B, C, M, N, K, out_dtype, FP8_BLOCK64);
+    if (st != FP8_OK) return st;
+    if (!s_a || !s_b) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
+    const int32_t T = (out_dtype & FP8_BLOCK64) ? 64 : 32;
+    if (M % T || N % T || K % T)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "M=%lld N=%lld K=%lld must be multiples of %d", (long long)M,
+                    (long long)N, (long long)K, T);
     if (M == 0 || N == 0) return ok();
-    return from_hip(fp8k::launch_gemm_blockscaled(A, B, s_a, s_b, C, M, N, K, out_dtype & 0xFF, (hipStream_t)stream),
+    return from_hip(fp8k::launch_gemm_blockscaled(A, B, s_a, s_b, C, M, N, K, out_dtype & 0xFF, T, (hipStream_t)stream),
                     "fp8_gemm_blockscaled");
 }
 
 fp8_status fp8_grouped_gemm(const uint8_t* A, const uint8_t* B, const int32_t* offsets, int32_t experts,
                             const float* scale_a, const float* scale_b, void* C, int64_t T, int64_t N, int64_t K,
                             int32_t out_dtype, void* stream) {
-    fp8_status st = check_gemm_common(A, B, C, T, N, K, out_dtype);
+    fp8_status st = check_gemm_common(A, B, C, T, N, K, out_dtype, FP8_ACC_FAST | FP8_A_E5M2 | FP8_B_E5M2);
     if (st != FP8_OK) return st;
     if (!scale_a || !scale_b || !offsets) return fail(FP8_ERR_INVALID_ARG, "null scale or offsets pointer");
     if (experts < 1 || experts > 1024) return fail(FP8_ERR_INVALID_ARG, "experts=%d outside [1, 1024]", experts);

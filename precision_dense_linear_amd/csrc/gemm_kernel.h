@@ -1,11 +1,12 @@
 // The FP8 GEMM tile loop for gfx950, instantiated by gemm.hip (per-tensor
 // and grouped GEMM: MODE_FAST, MODE_EXACT) and gemm_blockscaled.hip
-// (MODE_BLOCK).
+// (MODE_BLOCK, MODE_BLOCK64).
 //
 //   C[m, n] = (scale_a * scale_b) * sum_k A[m, k] * B[k, n]
 //
-// E4M3 operands, FP32 accumulation, the scales applied once to the finished
-// sum, FP32 or BF16 (RNE) output ("Triton FP8 GEMM via CUTLASS naming": kernel
+// E4M3 (or E5M2) operands, FP32 accumulation, the scales applied once to
+// the finished sum, FP32, BF16 or FP16 (RNE) output ("Triton FP8 GEMM via
+// CUTLASS naming": kernel
 // section, the paragraph after it and the parameter list).  A is M x K with K
 // contiguous and B is K x N with N contiguous, as in the kernel sketch of
 // "FP8 GEMM in JAX with Triton for Blackwell"; the grouped form runs the same
@@ -13,9 +14,11 @@
 // paragraph).
 //
 // The block-scaled form (32x32 tile scales, the parameter paragraph of "FP8
-// GEMM in JAX with Triton for Blackwell") runs the same tile loop and folds
-// each 32-deep K block's partial product into the FP32 accumulator with its
-// scale pair (the promotion step that page assigns to the CUDA cores).
+// GEMM in JAX with Triton for Blackwell"; 64x64 tiles, the coarser
+// granularity of its monitoring paragraph) runs the same tile loop and folds
+// each 32- or 64-deep K block's partial product into the FP32 accumulator
+// with its scale pair (the promotion step that page assigns to the CUDA
+// cores).
 //
 // Operand feed per 64-byte K slice: lane l (row or column l%32 of its 32-wide
 // block, lane group h = l/32) holds the 16-byte K chunks h and h+2 of the
@@ -59,19 +62,25 @@ __device__ __forceinline__ void static_for(F&& f) {
 enum Mode : int {
     MODE_FAST = 0,   // native FP8 MFMA (K=64)
     MODE_EXACT = 1,  // E4M3 widened exactly to BF16, K=16 BF16 MFMAs
-    MODE_BLOCK = 2,  // as MODE_EXACT, with a scale pair per 32x32 block and 32-deep K block
+    MODE_BLOCK = 2,    // as MODE_EXACT, with a scale pair per 32x32 block and 32-deep K block
+    MODE_BLOCK64 = 3,  // the same with 64x64 scale tiles and 64-deep K blocks (one per slice)
 };
 
 // FMT: operand formats, bit 0 set = A holds E5M2 codes, bit 1 = B (else E4M3).
 template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, bool BF16, int MODE, bool SPLITK = false,
           int FMT = 0>
 __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
-    static_assert(MODE != MODE_BLOCK || FMT == 0, "the block-scaled form takes E4M3 operands");
+    constexpr bool BLOCKED = MODE == MODE_BLOCK || MODE == MODE_BLOCK64;
+    constexpr int KBD = MODE == MODE_BLOCK64 ? 64 : 32;  // K depth and edge of a scale tile
+    constexpr int KB_PER_SLICE = BKP / KBD;             // scale blocks per 64-byte slice: 2 or 1
+    static_assert(!BLOCKED || FMT == 0, "the block-scaled form takes E4M3 operands");
     constexpr int FA = FMT & 1, FB = (FMT >> 1) & 1;
     using C = PipeCfg<BM, BN, WM, WN, KS, NB>;
     constexpr int TM = C::TM, TN = C::TN;
     constexpr bool WIDEN = MODE != MODE_FAST;
-    static_assert(MODE != MODE_BLOCK || KS == 1, "block scales need whole 32-deep K blocks per wave group");
+    static_assert(!BLOCKED || KS == 1, "block scales need whole K blocks per wave group");
+    static_assert(MODE != MODE_BLOCK64 || (C::WTM % 64 == 0 && C::WTN % 64 == 0),
+                  "a wave tile covers whole 64x64 scale tiles");
     constexpr int EPI = (KS > 1 ? C::RED : 0) + WM * WN * TileStore<BF16, TM, TN>::LDS_BYTES;
     static_assert(EPI <= 160 * 1024, "epilogue LDS budget");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS > EPI ? C::LDS : EPI];
@@ -172,47 +181,50 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int ni = 0; ni < TN; ++ni) bb[c & 1][ni] = fp8x8_to_bf16<FB>(f.b[ni][c][0], f.b[ni][c][1]);
     };
-    // MODE_BLOCK: the 32-deep K block's partial product per accumulator block
-    // (pieces 2kb and 2kb+1 of the slice), folded into acc with its scale.
-    v16f part[MODE == MODE_BLOCK ? TM : 1][MODE == MODE_BLOCK ? TN : 1];
+    // Block modes: the K block's partial product per accumulator block
+    // (pieces 2kb and 2kb+1 of the slice for 32-deep blocks, all four pieces
+    // for 64-deep ones), folded into acc with its scale.
+    v16f part[BLOCKED ? TM : 1][BLOCKED ? TN : 1];
     auto mfma_one = [&](auto m_c, const Frags<TM, TN>& f) {
         constexpr int m = decltype(m_c)::value;
         if constexpr (MODE == MODE_EXACT) {
             constexpr int c = m / BLK, mi = (m % BLK) / TN, ni = m % TN;
             acc[mi][ni] = mfma_32x32x16_bf16(bb[c & 1][ni], ab[c & 1][mi], acc[mi][ni]);
-        } else if constexpr (MODE == MODE_BLOCK) {
+        } else if constexpr (BLOCKED) {
             constexpr int c = m / BLK, mi = (m % BLK) / TN, ni = m % TN;
             const v16f zero = {};
-            part[mi][ni] = mfma_32x32x16_bf16(bb[c & 1][ni], ab[c & 1][mi], (c % 2 == 0) ? zero : part[mi][ni]);
+            constexpr bool first = MODE == MODE_BLOCK ? (c % 2 == 0) : (c == 0);  // first piece of its K block
+            part[mi][ni] = mfma_32x32x16_bf16(bb[c & 1][ni], ab[c & 1][mi], first ? zero : part[mi][ni]);
         } else {
             constexpr int mi = m / TN, ni = m % TN;
             acc[mi][ni] = mfma_32x32x64_f8<FB, FA>(b_op(f, ni), a_op(f, mi), acc[mi][ni]);
         }
     };
-    // MODE_BLOCK scale indices: tile-scale row of each A block and column of
-    // each B block (clamped: blocks past M or N are never stored), and the
-    // numbers of 32-deep K blocks and 32-wide column blocks.
+    // Block modes' scale indices: tile-scale row of each A block and column
+    // of each B block (clamped: blocks past M or N are never stored), and the
+    // numbers of KBD-deep K blocks and KBD-wide column blocks.
     int sa_row[TM], sb_col[TN];
-    const int64_t KBLK = K / 32, NBLK = N / 32;
-    if constexpr (MODE == MODE_BLOCK) {
+    const int64_t KBLK = K / KBD, NBLK = N / KBD;
+    if constexpr (BLOCKED) {
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
-            sa_row[mi] = (int)min<int64_t>((t.m0 + wm * C::WTM + mi * 32) / 32, t.M / 32 - 1);
+            sa_row[mi] = (int)min<int64_t>((t.m0 + wm * C::WTM + mi * 32) / KBD, t.M / KBD - 1);
 #pragma unroll
-        for (int ni = 0; ni < TN; ++ni) sb_col[ni] = (int)min<int64_t>((t.n0 + wn * C::WTN + ni * 32) / 32, NBLK - 1);
+        for (int ni = 0; ni < TN; ++ni)
+            sb_col[ni] = (int)min<int64_t>((t.n0 + wn * C::WTN + ni * 32) / KBD, NBLK - 1);
     }
-    // MODE_BLOCK tile scales: read through the constant address space, so
+    // Block modes' tile scales: read through the constant address space, so
     // they come in by scalar loads, counted by lgkmcnt rather than by the
     // vmcnt that tracks the stage loads, and one slice ahead, so the
     // lgkmcnt(0) wait at the next slice's barrier covers them.  sa_nx / sb_nx
-    // hold the scales of the next slice's two K blocks (clamped: past the end
-    // of K the partial products are zero).
+    // hold the scales of the next slice's K blocks (two 32-deep or one
+    // 64-deep; clamped: past the end of K the partial products are zero).
     typedef const __attribute__((address_space(4))) float cfloat;
     float sa_nx[2][TM], sb_nx[2][TN];
     auto load_slice_scales = [&](int64_t sl) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int64_t k = min<int64_t>(2 * sl + r, KBLK - 1);
+        for (int r = 0; r < KB_PER_SLICE; ++r) {
+            const int64_t k = min<int64_t>(KB_PER_SLICE * sl + r, KBLK - 1);
 #pragma unroll
             for (int mi = 0; mi < TM; ++mi) sa_nx[r][mi] = *(cfloat*)(p.scale_a + sa_row[mi] * KBLK + k);
 #pragma unroll
@@ -243,18 +255,20 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     // Spreading the loads between the MFMAs keeps the four waves from
     // queueing a whole stage of loads at once behind the barrier, which
     // stalls each wave's MFMA issue until the address unit has accepted them.
-    // In MODE_BLOCK a region is one 32-deep K block: its MFMAs, then the fold.
+    // In the block modes a region is half a slice (one 32-deep K block, or
+    // half of a 64-deep one): its MFMAs, then the fold at the end of each K
+    // block.
     // Loads past the end of K are empty (they read zero), so the body is
     // branch-free and the in-flight load count is the same every slice.  The
     // loop is unrolled over the NB B buffers (and fragment register pairs);
     // the slice count is a whole number of A stages, and rounded up to whole
     // loop bodies, the extra slices multiplying zeros (an accumulator that
     // starts at +0 stays exact under +0 terms).
-    constexpr int G = MODE == MODE_BLOCK ? 2 : C::LPS;  // regions per slice
+    constexpr int G = BLOCKED ? 2 : C::LPS;  // regions per slice
     constexpr int U = NB;                               // slices per unrolled body
     static_assert(U % 2 == 0, "fragment register pairs and A-stage halves alternate");
     Frags<TM, TN> f0, f1;
-    if constexpr (MODE == MODE_BLOCK) load_slice_scales(0);
+    if constexpr (BLOCKED) load_slice_scales(0);
     loader.issue_a_half(-NB - 1);
 #pragma unroll
     for (int s = -NB; s < 0; ++s) loader.issue_slice(s);
@@ -273,12 +287,12 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
             wait_vmcnt_lds<(NB - 2) * C::LPS>();
             __syncthreads();
             const typename Loader::Stage stage = loader.prepare(s);
-            // MODE_BLOCK: this slice's scales (loaded one slice ago), then the
-            // next slice's
+            // block modes: this slice's scales (loaded one slice ago), then
+            // the next slice's
             float sa_cur[2][TM], sb_cur[2][TN];
-            if constexpr (MODE == MODE_BLOCK) {
+            if constexpr (BLOCKED) {
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
+                for (int r = 0; r < KB_PER_SLICE; ++r) {
 #pragma unroll
                     for (int mi = 0; mi < TM; ++mi) sa_cur[r][mi] = sa_nx[r][mi];
 #pragma unroll
@@ -308,20 +322,23 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
                              abuf, next);
                 });
                 constexpr int nq = q1 - q0, nm = m1 - m0;
-                if constexpr (MODE == MODE_BLOCK) {
-                    // K block 2s + r: pieces 2r and 2r+1 into each block's
-                    // partial, then the fold of each block (each depends only
-                    // on its own block's last MFMA, so the scheduler can
-                    // overlap it with the other blocks' MFMAs)
+                if constexpr (BLOCKED) {
+                    // pieces 2r and 2r+1 into each block's partial; a K block
+                    // ends with this region in MODE_BLOCK (block 2s + r) and
+                    // with region 1 in MODE_BLOCK64 (block s): then the fold
+                    // of each accumulator block (each depends only on its own
+                    // block's last MFMA, so the scheduler can overlap it with
+                    // the other blocks' MFMAs)
                     convert(std::integral_constant<int, 2 * r>{}, cur);
                     convert(std::integral_constant<int, 2 * r + 1>{}, cur);
                     static_for<m0, m1>([&](auto m_c) { mfma_one(m_c, cur); });
-                    fold(sa_cur[r], sb_cur[r]);
+                    if constexpr (MODE == MODE_BLOCK) fold(sa_cur[r], sb_cur[r]);
+                    else if constexpr (r == 1) fold(sa_cur[0], sb_cur[0]);
                 } else {
                     static_for<m0, m1>([&](auto m_c) { mfma_one(m_c, cur); });
                 }
                 // interleave the region's LDS reads with its MFMAs
-                if constexpr (MODE != MODE_BLOCK && nm > 0 && nq > 0) {
+                if constexpr (!BLOCKED && nm > 0 && nq > 0) {
                     constexpr int RPM = (nq + nm - 1) / nm;
 #pragma unroll
                     for (int g = 0; g < (nq + RPM - 1) / RPM; ++g) {
@@ -437,7 +454,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     if constexpr (KS == 1) __syncthreads();
     using Store = TileStore<BF16, TM, TN>;
     lds_u8* scratch = lds + (KS > 1 ? C::RED : 0) + (wm * WN + wn) * Store::LDS_BYTES;
-    const float scale = MODE == MODE_BLOCK ? 1.0f : p.scale_a[t.expert] * p.scale_b[t.expert];
+    const float scale = BLOCKED ? 1.0f : p.scale_a[t.expert] * p.scale_b[t.expert];
     Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch,
                p.out_f16 != 0);
 }

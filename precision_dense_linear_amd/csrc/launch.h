@@ -11,7 +11,8 @@ namespace fp8k {
 // fmt: 0 = E4M3, 1 = E5M2
 hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, int fmt,
                                      hipStream_t s);
-hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* tile_scales,
+// T x T tiles, T = 32 or 64
+hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, int T, uint8_t* q, float* tile_scales,
                                    hipStream_t s);
 hipError_t launch_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
                                    uint8_t* q, float* scales, float* amax, int fmt, hipStream_t s);
@@ -40,8 +41,8 @@ hipError_t launch_gemm_fmt1(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_fmt2(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_fmt3(const GemmProblem& p, hipStream_t s);
 
-// out: 0 FP32, 1 BF16, 2 FP16
+// out: 0 FP32, 1 BF16, 2 FP16; block: edge of the scale tiles, 32 or 64
 hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,
-                                   int64_t M, int64_t N, int64_t K, int32_t out, hipStream_t s);
+                                   int64_t M, int64_t N, int64_t K, int32_t out, int32_t block, hipStream_t s);
 
 }  // namespace fp8k

@@ -6,7 +6,9 @@
 // parameter list); 32x32 block scales follow the parameter paragraph of "FP8
 // GEMM in JAX with Triton for Blackwell", whose opening section also names
 // the E5M2 format.  In every mode, with FMAX = 448 (E4M3) or 57344 (E5M2,
-// per-tensor and row-group quantization only):
+// per-tensor and row-group quantization only; block scales of 32x32 or 64x64
+// tiles, the latter the coarser granularity of that page's monitoring
+// paragraph, are E4M3):
 //     scale = amax / FMAX (IEEE binary32 division, 1 for amax == 0)
 //     code  = RNE(clamp(fl32(x / scale), -FMAX, FMAX))
 // All kernels are HBM-bound streams: 16-byte loads, 16-byte code stores.
@@ -108,34 +110,39 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restr
         for (int64_t j = (n4 << 2) + threadIdx.x; j < n; j += blockDim.x) q[j] = fp8_sat<F>(__fdiv_rn(x[j], s));
 }
 
-// 32x32 tiles: one wave per tile.  Load j of lane l covers tile row
-// 8j + l/8, columns 4(l%8) .. +3, so each of the four load instructions reads
-// eight whole 128-byte row segments; amax over the tile by a wave reduction,
-// then the codes (a 32-byte run per row and instruction).
+// T x T tiles (T = 32 or 64): one wave per tile.  A row of the tile is T/4
+// lanes of four floats (LPR lanes); load j of lane l covers tile row
+// (64/LPR) j + l/LPR, columns 4(l%LPR) .. +3, so each load instruction reads
+// whole 4T-byte row segments.  amax over the tile by a wave reduction, then
+// the codes (a T-byte run per row and instruction).
+template <int T>
 __global__ void __launch_bounds__(kThreads) quantize_blocked_kernel(const float* __restrict__ x, int64_t rows,
                                                                     int64_t cols, uint8_t* __restrict__ q,
                                                                     float* __restrict__ tile_scales) {
-    const int64_t tiles_c = cols >> 5;
-    const int64_t ntiles = (rows >> 5) * tiles_c;
+    constexpr int LPR = T / 4;        // lanes per tile row
+    constexpr int RPI = 64 / LPR;     // tile rows per load instruction
+    constexpr int NL = T / RPI;       // loads per lane
+    const int64_t tiles_c = cols / T;
+    const int64_t ntiles = (rows / T) * tiles_c;
     const int lane = threadIdx.x & 63;
     const int64_t tile = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (tile >= ntiles) return;
     const int64_t ti = tile / tiles_c, tj = tile % tiles_c;
-    const int64_t r = ti * 32 + (lane >> 3);
-    const int64_t c = tj * 32 + (lane & 7) * 4;
-    v4f v[4];
+    const int64_t r = ti * T + lane / LPR;
+    const int64_t c = tj * T + (lane % LPR) * 4;
+    v4f v[NL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        v[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(x + (r + 8 * j) * cols + c));
+    for (int j = 0; j < NL; ++j)
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(x + (r + RPI * j) * cols + c));
     float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+    for (int j = 0; j < NL; ++j) m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
     m = wave_max(m);
     const float s = scale_from_amax(m);
     if (lane == 0) tile_scales[tile] = s;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint32_t*>(q + (r + 8 * j) * cols + c) =
+    for (int j = 0; j < NL; ++j)
+        *reinterpret_cast<uint32_t*>(q + (r + RPI * j) * cols + c) =
             e4m3x4_sat(__fdiv_rn(v[j].x, s), __fdiv_rn(v[j].y, s), __fdiv_rn(v[j].z, s), __fdiv_rn(v[j].w, s));
 }
 
@@ -274,13 +281,17 @@ hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, floa
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* tile_scales,
+hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, int T, uint8_t* q, float* tile_scales,
                                    hipStream_t s) {
-    const int64_t ntiles = (rows / 32) * (cols / 32);
+    const int64_t ntiles = (rows / T) * (cols / T);
     if (ntiles == 0) return hipSuccess;
     const int64_t blocks = (ntiles + kThreads / 64 - 1) / (kThreads / 64);
-    hipLaunchKernelGGL(quantize_blocked_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, rows, cols, q,
-                       tile_scales);
+    if (T == 64)
+        hipLaunchKernelGGL(quantize_blocked_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, rows, cols, q,
+                           tile_scales);
+    else
+        hipLaunchKernelGGL(quantize_blocked_kernel<32>, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, rows, cols, q,
+                           tile_scales);
     return hipGetLastError();
 }
 

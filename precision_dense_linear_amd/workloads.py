@@ -60,21 +60,23 @@ def llm_linear(M: int, N: int, K: int, seed: int = 0, outlier_gain: float = 20.0
     return a, w
 
 
-def tile_factors(rows: int, cols: int, seed: int, name: str, lo: float = -2.0, hi: float = 2.0) -> np.ndarray:
-    """One factor 10^U(lo, hi) per 32 x 32 tile: float32[rows/32, cols/32]."""
-    u = rng(seed, name + "-tiles").uniform(lo, hi, size=(rows // 32, cols // 32))
+def tile_factors(rows: int, cols: int, seed: int, name: str, lo: float = -2.0, hi: float = 2.0,
+                 tile: int = 32) -> np.ndarray:
+    """One factor 10^U(lo, hi) per tile x tile tile: float32[rows/tile, cols/tile]."""
+    u = rng(seed, name + "-tiles" + ("" if tile == 32 else "%d" % tile)).uniform(lo, hi,
+                                                                              size=(rows // tile, cols // tile))
     return np.power(10.0, u).astype(np.float32)
 
 
-def expand_tiles(f: np.ndarray) -> np.ndarray:
-    return np.repeat(np.repeat(f, 32, axis=0), 32, axis=1)
+def expand_tiles(f: np.ndarray, tile: int = 32) -> np.ndarray:
+    return np.repeat(np.repeat(f, tile, axis=0), tile, axis=1)
 
 
-def blockscaled_pair(M: int, N: int, K: int, seed: int = 0):
-    """A, B N(0,1), each 32x32 tile times its own log-uniform factor in [1e-2, 1e2]."""
+def blockscaled_pair(M: int, N: int, K: int, seed: int = 0, tile: int = 32):
+    """A, B N(0,1), each tile x tile tile (32 or 64) times its own log-uniform factor in [1e-2, 1e2]."""
     a, b = pertensor_pair(M, N, K, seed)
-    a *= expand_tiles(tile_factors(M, K, seed, "A"))
-    b *= expand_tiles(tile_factors(K, N, seed, "B"))
+    a *= expand_tiles(tile_factors(M, K, seed, "A", tile=tile), tile)
+    b *= expand_tiles(tile_factors(K, N, seed, "B", tile=tile), tile)
     return a, b
 
 

@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_grouped",
+    for n in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
+              "fp8_quantize_grouped",
               "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
               "fp8_status_string", "fp8_last_error"):
         assert n in names
@@ -85,6 +86,12 @@ def test_blockscaled_validation():
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 2, None) == P.FP8_OK                 # FP16 out
     for flag in (P.FP8_A_E5M2, P.FP8_B_E5M2, P.FP8_ACC_FAST):                              # E4M3, exact only
         assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 1 | flag, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 96, 64, 64, 1 | P.FP8_BLOCK64, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 96, 1 | P.FP8_BLOCK64, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 2 | P.FP8_BLOCK64, None) == P.FP8_OK
+    assert gemm(out=1 | P.FP8_BLOCK64) == P.FP8_ERR_INVALID_ARG                           # block-scaled only
+    assert P.lib.fp8_grouped_gemm(FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, 64, 64, 64, 1 | P.FP8_BLOCK64, None) \
+        == P.FP8_ERR_INVALID_ARG
 
 
 def test_grouped_validation():
@@ -108,6 +115,9 @@ def test_quantize_validation():
         == P.FP8_ERR_INVALID_ARG
     assert L.fp8_quantize_blocked(FAKE, 48, 64, FAKE, FAKE, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
     assert L.fp8_quantize_blocked(FAKE, 64, 64, None, FAKE, None) == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize_blocked64(FAKE, 96, 64, FAKE, FAKE, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert L.fp8_quantize_blocked64(FAKE, 64, 64, None, FAKE, None) == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize_blocked64(FAKE, 0, 64, FAKE, FAKE, None) == P.FP8_OK
     assert L.fp8_quantize_grouped(FAKE, 64, 64, FAKE, 0, FAKE, FAKE, ctypes.c_void_p(0x200000), None) \
         == P.FP8_ERR_INVALID_ARG
     assert L.fp8_quantize_grouped(FAKE, 64, 6, FAKE, 2, FAKE, FAKE, ctypes.c_void_p(0x200000), None) \

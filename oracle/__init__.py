@@ -22,6 +22,9 @@ paragraph -- grouped GEMM over experts):
 * ``quantize_blocked_t`` / ``gemm_blockscaled_rows_t`` -- block scales of
                           32x32 or 64x64 tiles (the Blackwell page's
                           granularity and its coarser fallback).
+* ``quantize_blocked_e8m0`` / ``gemm_blockscaled_e8m0_rows`` -- 32x32 tile
+                          scales as powers of two (OCP MX shared exponents,
+                          E8M0 bytes).
 * ``e5m2_table``, ``quantize_*_fmt``, ``gemm_rows_fmt`` -- the same for OCP
                           E5M2 operands (scale = fl32(amax/57344)) and mixed
                           E4M3 x E5M2 pairs, summed exactly in 128-bit
@@ -106,6 +109,10 @@ def lib():
                                         P, P, P]
         L.orc_quantize_blocked_t.argtypes = [P, i64, i64, ctypes.c_int, P, P]
         L.orc_gemm_blockscaled_rows_t.argtypes = [P, P, P, P, i64, i64, ctypes.c_int, P, i64, ctypes.c_int, P, P, P]
+        L.orc_e8m0_exponent.restype = ctypes.c_int
+        L.orc_e8m0_exponent.argtypes = [f32]
+        L.orc_quantize_blocked_e8m0.argtypes = [P, i64, i64, P, P]
+        L.orc_gemm_blockscaled_e8m0_rows.argtypes = [P, P, P, P, i64, i64, P, i64, ctypes.c_int, P, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -454,4 +461,44 @@ def gemm_blockscaled_rows_t(qa, qb, s_a, s_b, T, kind, rows=None):
     sab = np.empty((nr, N), np.float64)
     lib().orc_gemm_blockscaled_rows_t(_p(qa), _p(qb), _p(s_a), _p(s_b), N, K, T, _p(rows), nr, kind, _p(out),
                                       _p(exact), _p(sab))
+    return (out if kind == F32 else out.astype(np.uint16)), exact, sab
+
+
+# --------------------------------------------------------------------------
+# 32x32 block scales as powers of two (E8M0 bytes): the Blackwell page's
+# 32x32 microscaling with OCP MX shared exponents
+# --------------------------------------------------------------------------
+def e8m0_exponent(amax: float) -> int:
+    """Shared exponent floor(log2(amax)) - 8, clamped to [-127, 127]; 0 for amax 0."""
+    return int(lib().orc_e8m0_exponent(ctypes.c_float(amax)))
+
+
+def quantize_blocked_e8m0(x: np.ndarray):
+    """32x32 tiles; returns (codes, E8M0 bytes uint8[rows/32, cols/32])."""
+    x = _c(x, np.float32)
+    rows, cols = x.shape
+    assert rows % 32 == 0 and cols % 32 == 0
+    q = np.empty(x.shape, dtype=np.uint8)
+    sc = np.empty((rows // 32, cols // 32), dtype=np.uint8)
+    lib().orc_quantize_blocked_e8m0(_p(x), rows, cols, _p(q), _p(sc))
+    return q, sc
+
+
+def gemm_blockscaled_e8m0_rows(qa, qb, s_a, s_b, kind, rows=None):
+    """GEMM with E8M0 32x32 tile scales on the selected rows: (bits, FP64 sum, scaled sumabs)."""
+    qa = _c(qa, np.uint8)
+    qb = _c(qb, np.uint8)
+    s_a = _c(s_a, np.uint8)
+    s_b = _c(s_b, np.uint8)
+    M, K = qa.shape
+    N = qb.shape[1]
+    assert M % 32 == 0 and N % 32 == 0 and K % 32 == 0
+    assert s_a.shape == (M // 32, K // 32) and s_b.shape == (K // 32, N // 32)
+    rows = np.arange(M, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    nr = rows.size
+    out = np.empty((nr, N), np.uint32)
+    exact = np.empty((nr, N), np.float64)
+    sab = np.empty((nr, N), np.float64)
+    lib().orc_gemm_blockscaled_e8m0_rows(_p(qa), _p(qb), _p(s_a), _p(s_b), N, K, _p(rows), nr, kind, _p(out),
+                                         _p(exact), _p(sab))
     return (out if kind == F32 else out.astype(np.uint16)), exact, sab

@@ -725,3 +725,100 @@ void orc_gemm_blockscaled_rows_t(const uint8_t* A, const uint8_t* B, const float
         free(apart);
     }
 }
+
+/* ======================================================================== */
+/* 32x32 block scales as powers of two (E8M0), applied by the matrix cores:  */
+/* the microscaling of "FP8 GEMM in JAX with Triton for Blackwell"           */
+/* (parameter paragraph: 32x32 scale blocks) with each scale an 8-bit        */
+/* exponent, as the OCP microscaling formats store it.  Reading (the page    */
+/* gives only the granularity): the shared exponent of a tile follows the    */
+/* OCP MX conversion for an E4M3 element type -- e = floor(log2(amax)) - 8  */
+/* (8: the largest E4M3 exponent), clamped to [-127, 127], stored as the     */
+/* byte e + 127; the codes are RNE_SAT(fl32(x / 2^e)), saturating at +-448   */
+/* (amax / 2^e lies in [256, 512)).  An all-zero tile stores e = 0 (127).    */
+/* ======================================================================== */
+
+/* Shared exponent of a tile from its amax (finite, >= 0). */
+int orc_e8m0_exponent(float amax) {
+    if (amax == 0.0f) return 0;
+    int ex;
+    frexp((double)amax, &ex);          /* amax = f * 2^ex, 0.5 <= f < 1: floor(log2 amax) = ex - 1 */
+    int e = (ex - 1) - 8;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* 32x32 tiles (rows, cols multiples of 32): codes and one E8M0 byte per tile,
+ * row-major [rows/32][cols/32]. */
+void orc_quantize_blocked_e8m0(const float* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scales) {
+    int64_t tr = rows / 32, tc = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < tr * tc; t++) {
+        int64_t bi = t / tc, bj = t % tc;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < 32; i++)
+            for (int64_t j = 0; j < 32; j++) {
+                float a = fabsf(x[(bi * 32 + i) * cols + bj * 32 + j]);
+                if (a > amax) amax = a;
+            }
+        int e = orc_e8m0_exponent(amax);
+        scales[t] = (uint8_t)(e + 127);
+        float X = ldexpf(1.0f, e);   /* 2^e: 2^-127 is a binary32 subnormal, still exact */
+        for (int64_t i = 0; i < 32; i++)
+            for (int64_t j = 0; j < 32; j++) {
+                int64_t idx = (bi * 32 + i) * cols + bj * 32 + j;
+                volatile float quot = x[idx] / X;
+                q[idx] = orc_e4m3_rne_sat(quot);
+            }
+    }
+}
+
+/* GEMM with E8M0 tile scales on a set of rows:
+ *   C[i,j] = sum_kb 2^(ea[i/32,kb] + eb[kb,j/32]) * sum_{k in block kb} a[i,k]*b[k,j]
+ * (ea, eb = byte - 127); each block sum is exact and scaling by a power of two
+ * is exact, the sum over blocks is taken in FP64, rounded once (kind 0 / 1 /
+ * 2: FP32 / BF16 / FP16; one uint32 of bits per output).  exact receives the
+ * FP64 sum, sabs sum_kb 2^(ea+eb) * sum_k |a*b|. */
+void orc_gemm_blockscaled_e8m0_rows(const uint8_t* A, const uint8_t* B, const uint8_t* s_a, const uint8_t* s_b,
+                                    int64_t N, int64_t K, const int64_t* rows, int64_t nr, int kind,
+                                    uint32_t* out, double* exact, double* sabs) {
+    double tab[256];
+    orc_e4m3_table(tab);
+    for (int c = 0; c < 256; c++) if (isnan(tab[c])) tab[c] = 0.0;
+    int64_t KB = K / 32, NBT = N / 32;
+#pragma omp parallel
+    {
+        double* part = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double* apart = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nr; r++) {
+            int64_t i = rows[r];
+            double* crow = exact + r * N;
+            double* srow = sabs + r * N;
+            for (int64_t j = 0; j < N; j++) { crow[j] = 0.0; srow[j] = 0.0; }
+            for (int64_t kb = 0; kb < KB; kb++) {
+                for (int64_t j = 0; j < N; j++) { part[j] = 0.0; apart[j] = 0.0; }
+                for (int64_t k = kb * 32; k < kb * 32 + 32; k++) {
+                    double a = tab[A[i * K + k]];
+                    if (a == 0.0) continue;
+                    const uint8_t* brow = B + k * N;
+                    for (int64_t j = 0; j < N; j++) {
+                        double p = a * tab[brow[j]];
+                        part[j] += p;
+                        apart[j] += fabs(p);
+                    }
+                }
+                int ea = (int)s_a[(i / 32) * KB + kb] - 127;
+                for (int64_t j = 0; j < N; j++) {
+                    int e = ea + (int)s_b[kb * NBT + j / 32] - 127;
+                    crow[j] += ldexp(part[j], e);
+                    srow[j] += ldexp(apart[j], e);
+                }
+            }
+            for (int64_t j = 0; j < N; j++) out[r * N + j] = orc_round_ieee_f64(crow[j], kind);
+        }
+        free(part);
+        free(apart);
+    }
+}

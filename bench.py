@@ -114,7 +114,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gemm8192",
                     choices=["gemm8192", "gemm1024", "gemm256", "llm16", "llm128", "llm4096", "blockscaled8192",
-                             "moe", "mixed8192", "blockscaled8192_64"])
+                             "moe", "mixed8192", "blockscaled8192_64", "blockscaled8192_e8m0"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy twice (reference for the HBM byte counters)")
@@ -158,6 +158,12 @@ class Workload:
             a, b = W.llm_linear(self.M, self.N, self.K)
             self.desc = ("LLM linear layer M=%d N=%d K=%d, per-tensor FP8, BF16 out; activations N(0,1) with 1%% "
                          "outlier channels x20, weights N(0,0.02)" % (self.M, self.N, self.K))
+        elif name == "blockscaled8192_e8m0":
+            self.kind = "block_e8"
+            self.M = self.N = self.K = 8192
+            a, b = W.blockscaled_pair(8192, 8192, 8192)
+            self.desc = ("block-scaled FP8 GEMM M=N=K=8192 with power-of-two (E8M0) 32x32 tile scales applied by the "
+                         "FP8 matrix cores, BF16 out; tile factors 10^U(-2,2)")
         elif name.startswith("blockscaled8192"):
             self.kind = "block"
             self.block = 64 if name.endswith("_64") else 32
@@ -183,6 +189,10 @@ class Workload:
         if self.kind == "pertensor":
             self.sa, self.aa = (torch.empty(1, device=dev) for _ in range(2))
             self.sb, self.ab = (torch.empty(1, device=dev) for _ in range(2))
+        elif self.kind == "block_e8":
+            pitch = lambda n: (n + 3) // 4 * 4
+            self.sa = torch.empty((self.K // 32, pitch(self.M // 32)), dtype=torch.uint8, device=dev)
+            self.sb = torch.empty((self.K // 32, pitch(self.N // 32)), dtype=torch.uint8, device=dev)
         elif self.kind == "block":
             self.sa = torch.empty((self.M // self.block, self.K // self.block), device=dev)
             self.sb = torch.empty((self.K // self.block, self.N // self.block), device=dev)
@@ -196,6 +206,9 @@ class Workload:
         if self.kind == "pertensor":
             P.fp8_quantize(self.A, self.qa, self.sa, self.aa)
             (P.fp8_quantize_e5m2 if self.b_e5m2 else P.fp8_quantize)(self.B, self.qb, self.sb, self.ab)
+        elif self.kind == "block_e8":
+            P.fp8_quantize_blocked_e8m0(self.A, True, self.qa, self.sa)
+            P.fp8_quantize_blocked_e8m0(self.B, False, self.qb, self.sb)
         elif self.kind == "block":
             qb = P.fp8_quantize_blocked64 if self.block == 64 else P.fp8_quantize_blocked
             qb(self.A, self.qa, self.sa)
@@ -211,6 +224,8 @@ class Workload:
         if self.kind == "pertensor":
             P.fp8_gemm(qa, qb, self.sa, self.sb, self.out, C=self.C, fast=fast,
                        b_fmt="e5m2" if self.b_e5m2 else "e4m3")
+        elif self.kind == "block_e8":
+            P.fp8_gemm_blockscaled_e8m0(qa, qb, self.sa, self.sb, self.out, C=self.C)
         elif self.kind == "block":
             P.fp8_gemm_blockscaled(qa, qb, self.sa, self.sb, self.out, C=self.C, block=self.block)
         else:
@@ -228,6 +243,8 @@ class Workload:
             return self.M * self.K + self.E * self.K * self.N + self.M * self.N * osz
         t = getattr(self, "block", 32)
         extra = (self.M // t) * (self.K // t) * 4 + (self.K // t) * (self.N // t) * 4 if self.kind == "block" else 0
+        if self.kind == "block_e8":
+            extra = (self.M // 32) * (self.K // 32) + (self.K // 32) * (self.N // 32)
         return self.M * self.K + self.K * self.N + self.M * self.N * osz + extra
 
 
@@ -314,7 +331,7 @@ def main():
 
     # the native-FP8-accumulation GEMM (FP8_ACC_FAST), timed the same way, outside the timed region
     fast = None
-    if w.kind != "block":
+    if w.kind not in ("block", "block_e8"):
         for _ in range(3):
             w.gemm(fast=True)
         fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -366,7 +383,13 @@ def main():
             rounds * ncopy, ncopy, (ncopy * per) >> 20,
             ", > 2x the 256 MB MALL: operands from HBM" if ncopy * per > 512e6 else ": small enough to stay cached")
         del cp
-    if mfma_bound:
+    if mfma_bound and w.kind == "block_e8":
+        # power-of-two tile scales: the scaled FP8 matrix-core instructions
+        peak = FP8_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / peak, 4), "traffic": measured_traffic(args.workload),
+                "peak_basis": "dense FP8 MFMA (the scaled FP8 instructions apply the E8M0 tile scales)"}
+    elif mfma_bound:
         # the default (exact-product) kernels multiply on the BF16 matrix cores
         peak = BF16_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak, "unit": "TFLOP/s",
@@ -378,9 +401,12 @@ def main():
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args.workload),
                 "basis": rotation,
                 "in_step_avg_kernel_us": round(avg_gemm_ms * 1e3, 2)}
-    roof["kernel"] = "gemm_kernel (fp8_gemm)" if w.kind == "pertensor" else (
-        ("gemm_kernel MODE_BLOCK64 (fp8_gemm_blockscaled, 64x64 tiles)" if getattr(w, "block", 32) == 64 else
-         "gemm_kernel MODE_BLOCK (fp8_gemm_blockscaled)") if w.kind == "block" else "gemm_kernel (fp8_grouped_gemm)")
+    roof["kernel"] = {
+        "pertensor": "gemm_kernel (fp8_gemm)",
+        "block": ("gemm_kernel MODE_BLOCK64 (fp8_gemm_blockscaled, 64x64 tiles)" if getattr(w, "block", 32) == 64
+                  else "gemm_kernel MODE_BLOCK (fp8_gemm_blockscaled)"),
+        "block_e8": "gemm_kernel MODE_E8M0 (fp8_gemm_blockscaled_e8m0)",
+        "moe": "gemm_kernel (fp8_grouped_gemm)"}[w.kind]
     roof["avg_kernel_us"] = round((avg_gemm_ms if mfma_bound else hbm_ms) * 1e3, 2)
     mhz = sclk.mean_mhz()
     sclk_out = None

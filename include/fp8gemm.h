@@ -155,6 +155,22 @@ fp8_status fp8_quantize_blocked64(const float* x, int64_t rows, int64_t cols, ui
                                   void* stream);
 
 /*
+ * 32x32-tile quantization with power-of-two scales ([P3] parameter
+ * paragraph: 32x32 microscaling; the scale kept as an 8-bit exponent, OCP
+ * E8M0): for tile (bi, bj) with amax > 0, e = floor(log2(amax)) - 8 (8: the
+ * largest E4M3 exponent, so amax / 2^e lies in [256, 512)), clamped to
+ * [-127, 127]; e = 0 for an all-zero tile.  The tile's byte e + 127 goes to
+ * tile_exps[bi * pitch(cols/32) + bj] (k_major = 0: the layout for B, K x N)
+ * or tile_exps[bj * pitch(rows/32) + bi] (k_major = 1: for A, M x K, so that
+ * the exponents of one K block are contiguous), pitch(n) = n rounded up to a
+ * multiple of 4 (the padding bytes are written as 127); q = E4M3(fl32(x /
+ * 2^e)), round to nearest even, saturating at +-448.  rows, cols >= 0 and
+ * multiples of 32; x, q 16-byte aligned, tile_exps 4-byte aligned.
+ */
+fp8_status fp8_quantize_blocked_e8m0(const float* x, int64_t rows, int64_t cols, int32_t k_major, uint8_t* q,
+                                     uint8_t* tile_exps, void* stream);
+
+/*
  * Row-group quantization, one scale per group ([P3] MoE paragraph with the
  * per-tensor scaling of [P1] applied per expert): group g is rows
  * [offsets[g], offsets[g+1]) of the rows x cols matrix x;
@@ -219,6 +235,25 @@ fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, co
  */
 fp8_status fp8_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,
                                 int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream);
+
+/*
+ * Block-scaled FP8 GEMM with power-of-two 32x32 tile scales applied by the
+ * FP8 matrix cores ([P3] parameter paragraph: 32x32 microscaling):
+ *     C[m, n] = sum_kb 2^(e_a[kb, m/32] - 127) * 2^(e_b[kb, n/32] - 127)
+ *                      * sum_{k in [32kb, 32kb+32)} A[m, k] * B[k, n]
+ * e_a: K/32 rows of pitch(M/32) bytes, e_b: K/32 rows of pitch(N/32) bytes
+ * (both K-block-major, pitch(n) = n rounded up to a multiple of 4), on the
+ * device and 4-byte aligned, as fp8_quantize_blocked_e8m0 writes them
+ * (k_major = 1 for A, 0 for B).  The matrix cores scale
+ * each 32-deep block of products and sum them with the FP8_ACC_FAST
+ * arithmetic (groups of 8 products aligned to a 13-bit window, then FP32),
+ * at the full FP8 rate: |C - C_exact| <= (7 * 2^-13 + 2e-6) *
+ * sum_kb 2^(e_a+e_b-254) * sum_k |a*b| (plus the output rounding).
+ * out_dtype: FP8_OUT_F32, FP8_OUT_BF16 or FP8_OUT_F16 (no flags).
+ * M, N, K >= 0 and multiples of 32, K <= 2^23; A, B, C 16-byte aligned.
+ */
+fp8_status fp8_gemm_blockscaled_e8m0(const uint8_t* A, const uint8_t* B, const uint8_t* e_a, const uint8_t* e_b,
+                                     void* C, int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream);
 
 /*
  * MoE grouped FP8 GEMM ([P3] MoE paragraph: the GEMM extended to a grouped

@@ -11,10 +11,12 @@ Entry points (same names as the C ABI):
     fp8_quantize_e5m2(x)                     -> (q, scale, amax)
     fp8_quantize_blocked(x)                  -> (q, tile_scales)
     fp8_quantize_blocked64(x)                -> (q, tile_scales)
+    fp8_quantize_blocked_e8m0(x, k_major)    -> (q, tile_exps uint8)
     fp8_quantize_grouped(x, offsets)         -> (q, scales, amax)
     fp8_quantize_grouped_e5m2(x, offsets)    -> (q, scales, amax)
     fp8_gemm(A, B, scale_a, scale_b, out_dtype)
     fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype, block=32 | 64)
+    fp8_gemm_blockscaled_e8m0(A, B, e_a, e_b, out_dtype)
     fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype)
 FP8 codes are passed as torch.uint8 (E4M3 unless a_fmt / b_fmt say "e5m2"),
 torch.float8_e4m3fn or torch.float8_e5m2 tensors; out_dtype is
@@ -37,7 +39,7 @@ FP8_A_E5M2, FP8_B_E5M2 = 0x200, 0x400  # operand formats (default E4M3)
 FP8_BLOCK64 = 0x800  # 64x64 scale tiles for the block-scaled GEMM
 
 SYMBOLS = ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
-           "fp8_quantize_grouped",
+           "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_grouped",
            "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
            "fp8_status_string", "fp8_last_error")
 
@@ -59,13 +61,15 @@ def _load():
     L.fp8_quantize_e5m2.argtypes = [P, i64, P, P, P, P]
     L.fp8_quantize_blocked.argtypes = [P, i64, i64, P, P, P]
     L.fp8_quantize_blocked64.argtypes = [P, i64, i64, P, P, P]
+    L.fp8_quantize_blocked_e8m0.argtypes = [P, i64, i64, i32, P, P, P]
+    L.fp8_gemm_blockscaled_e8m0.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_quantize_grouped.argtypes = [P, i64, i64, P, i32, P, P, P, P]
     L.fp8_quantize_grouped_e5m2.argtypes = [P, i64, i64, P, i32, P, P, P, P]
     L.fp8_gemm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_gemm_blockscaled.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i64, i64, i64, i32, P]
     for f in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
-              "fp8_quantize_grouped",
+              "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_grouped",
               "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
         getattr(L, f).restype = st
     L.fp8_status_string.restype = ctypes.c_char_p
@@ -175,6 +179,27 @@ def fp8_quantize_blocked64(x: torch.Tensor, q=None, tile_scales=None, stream=Non
     return _quantize_blocked("fp8_quantize_blocked64", 64, x, q, tile_scales, stream)
 
 
+def fp8_quantize_blocked_e8m0(x: torch.Tensor, k_major=False, q=None, tile_exps=None, stream=None):
+    """32x32-tile E4M3 quantization with power-of-two scales; returns (q, tile_exps uint8), tile_exps
+    holding e + 127 for the tile scale 2^e, shaped [rows/32, pitch(cols/32)], or [cols/32, pitch(rows/32)]
+    with k_major (the layout fp8_gemm_blockscaled_e8m0 takes for A); pitch(n) rounds n up to a multiple
+    of 4, the padding bytes hold 127."""
+    _require(x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 2,
+             "x must be a contiguous 2-D float32 GPU tensor")
+    rows, cols = x.shape
+    dev = x.device
+    q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else q
+    if tile_exps is None:
+        pitch = lambda n: (n + 3) // 4 * 4
+        shape = (cols // 32, pitch(rows // 32)) if k_major else (rows // 32, pitch(cols // 32))
+        tile_exps = torch.empty(shape, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check("fp8_quantize_blocked_e8m0", lib.fp8_quantize_blocked_e8m0(_ptr(x), rows, cols, int(bool(k_major)),
+                                                                          _ptr(q), _ptr(tile_exps),
+                                                                          _stream(dev, stream)))
+    return q, tile_exps
+
+
 def _quantize_grouped(func: str, x, offsets, q, scales, amax, stream):
     _require(x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 2,
              "x must be a contiguous 2-D float32 GPU tensor")
@@ -242,6 +267,24 @@ def fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype=torch.bfloat16, C=None, strea
         _check("fp8_gemm_blockscaled", lib.fp8_gemm_blockscaled(_ptr(A), _ptr(B), _ptr(s_a), _ptr(s_b), _ptr(C),
                                                                 M, N, K, code | (FP8_BLOCK64 if block == 64 else 0),
                                                                 _stream(A.device, stream)))
+    return C
+
+
+def fp8_gemm_blockscaled_e8m0(A, B, e_a, e_b, out_dtype=torch.bfloat16, C=None, stream=None):
+    """C = sum over 32-deep K blocks of 2^(e_a-127) * 2^(e_b-127) * (A_kb @ B_kb) on the FP8 matrix cores
+    (32x32 tile exponents, e_a [K/32, pitch(M/32)] and e_b [K/32, pitch(N/32)]; E4M3 operands)."""
+    _require(_fmt_flag(A, None, 1) == 0 and _fmt_flag(B, None, 1) == 0, "E4M3 operands only")
+    _require(e_a.dtype == torch.uint8 and e_b.dtype == torch.uint8, "tile exponents must be uint8 tensors")
+    A, B = _codes(A), _codes(B)
+    M, K = A.shape
+    N = B.shape[1]
+    _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
+    code = _out_code(out_dtype)
+    C = _out_tensor(C, (M, N), code, A.device)
+    with torch.cuda.device(A.device):
+        _check("fp8_gemm_blockscaled_e8m0", lib.fp8_gemm_blockscaled_e8m0(_ptr(A), _ptr(B), _ptr(e_a), _ptr(e_b),
+                                                                          _ptr(C), M, N, K, code,
+                                                                          _stream(A.device, stream)))
     return C
 
 

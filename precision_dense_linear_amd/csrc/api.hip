@@ -136,6 +136,21 @@ fp8_status fp8_quantize_blocked64(const float* x, int64_t rows, int64_t cols, ui
     return quantize_blocked(x, rows, cols, 64, q, tile_scales, stream, "fp8_quantize_blocked64");
 }
 
+fp8_status fp8_quantize_blocked_e8m0(const float* x, int64_t rows, int64_t cols, int32_t k_major, uint8_t* q,
+                                     uint8_t* tile_exps, void* stream) {
+    if (!x || !q || !tile_exps) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
+    if (k_major != 0 && k_major != 1) return fail(FP8_ERR_INVALID_ARG, "k_major=%d is neither 0 nor 1", k_major);
+    if ((uintptr_t)tile_exps & 3) return fail(FP8_ERR_INVALID_ARG, "tile_exps must be 4-byte aligned");
+    if (rows < 0 || cols < 0) return fail(FP8_ERR_INVALID_ARG, "negative size");
+    if (rows % 32 || cols % 32)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "rows=%lld and cols=%lld must be multiples of 32", (long long)rows,
+                    (long long)cols);
+    if (!aligned16(x) || !aligned16(q)) return fail(FP8_ERR_INVALID_ARG, "x and q must be 16-byte aligned");
+    if ((rows / 32) * (cols / 32) > (int64_t(1) << 34)) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "too many tiles");
+    return from_hip(fp8k::launch_quantize_blocked_e8m0(x, rows, cols, q, tile_exps, k_major, (hipStream_t)stream),
+                    "fp8_quantize_blocked_e8m0");
+}
+
 fp8_status fp8_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
                                 uint8_t* q, float* scales, float* amax, void* stream) {
     return quantize_grouped(x, rows, cols, offsets, groups, q, scales, amax, 0, stream, "fp8_quantize_grouped");
@@ -175,6 +190,22 @@ fp8_status fp8_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float*
     if (M == 0 || N == 0) return ok();
     return from_hip(fp8k::launch_gemm_blockscaled(A, B, s_a, s_b, C, M, N, K, out_dtype & 0xFF, T, (hipStream_t)stream),
                     "fp8_gemm_blockscaled");
+}
+
+fp8_status fp8_gemm_blockscaled_e8m0(const uint8_t* A, const uint8_t* B, const uint8_t* e_a, const uint8_t* e_b,
+                                     void* C, int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
+    fp8_status st = check_gemm_common(A, B, C, M, N, K, out_dtype, 0);
+    if (st != FP8_OK) return st;
+    if ((!e_a || !e_b) && K > 0) return fail(FP8_ERR_INVALID_ARG, "null exponent pointer");  // empty when K == 0
+    if (((uintptr_t)e_a & 3) || ((uintptr_t)e_b & 3))
+        return fail(FP8_ERR_INVALID_ARG, "the exponent arrays must be 4-byte aligned");
+    if (M % 32 || N % 32 || K % 32)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "M=%lld N=%lld K=%lld must be multiples of 32", (long long)M,
+                    (long long)N, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    return from_hip(
+        fp8k::launch_gemm_blockscaled_e8m0(A, B, e_a, e_b, C, M, N, K, out_dtype & 0xFF, (hipStream_t)stream),
+        "fp8_gemm_blockscaled_e8m0");
 }
 
 fp8_status fp8_grouped_gemm(const uint8_t* A, const uint8_t* B, const int32_t* offsets, int32_t experts,

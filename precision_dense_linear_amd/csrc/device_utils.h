@@ -34,12 +34,24 @@ __device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
 // (v_mfma_f32_32x32x64_f8f6f4; zero scale operands select the unscaled
 // form).  The operand formats are given per operand: 0 = E4M3, 1 = E5M2 (the
 // cbsz / blgp fields select the format of the first / second source).
-// Lane l holds A row l%32 / B column l%32, K positions 32*(l/32) .. +31 of
-// the instruction;
+// Lane l (h = l/32) holds A row l%32 / B column l%32: bytes 0-15 are K
+// positions 16h .. 16h+15 of the instruction, bytes 16-31 K positions
+// 32+16h .. 32+16h+15 (checked through the scaled form below, whose
+// 32-deep K blocks are K 0-31 and 32-63);
 // accumulator element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 template <int FMT_SRC0, int FMT_SRC1>
 __device__ __forceinline__ v16f mfma_32x32x64_f8(v8i a, v8i b, v16f c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT_SRC0, FMT_SRC1, 0, 0, 0, 0);
+}
+
+// The scaled form with E4M3 operands: the products of 32-deep K block b
+// (instruction K 0-31 or 32-63) of row / column i are multiplied by
+// 2^(e - 127), e the byte BYTE0 (BYTE1) of the scale operand of lane
+// 32b + i for the first (second) source (OCP E8M0; the op_sel field picks
+// the byte).
+template <int BYTE0, int BYTE1>
+__device__ __forceinline__ v16f mfma_32x32x64_e4m3_scaled(v8i a, v8i b, v16f c, int e8_src0, int e8_src1) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, BYTE0, e8_src0, BYTE1, e8_src1);
 }
 
 // D = A(32x16) * B(16x32) + C in BF16 with FP32 accumulate

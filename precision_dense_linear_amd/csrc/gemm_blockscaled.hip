@@ -27,6 +27,7 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const flo
     g.out_f16 = out == 2;
     g.fast_acc = 0;
     g.fmt = 0;
+    if (K == 0) return fill_zero(C, M * N * (out == 0 ? 4 : 2), s);  // empty sums: C = 0
     if (block == 64) return launch_mode<128, 128, 2, 2, 1, 4, 8, MODE_BLOCK64>(g, s);
     return launch_mode<128, 128, 2, 2, 1, 4, 8, MODE_BLOCK>(g, s);
 }

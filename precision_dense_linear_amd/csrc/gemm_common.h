@@ -30,6 +30,8 @@ struct GemmArgs {
     float* ws;
     uint32_t* counters;
     int32_t out_f16;  // 2-byte output is IEEE binary16 rather than BF16
+    const uint8_t* e8_a;  // E8M0 tile exponents of A [K/32][M/32] (MODE_E8M0 only)
+    const uint8_t* e8_b;  // E8M0 tile exponents of B [K/32][N/32]
 };
 
 // B stage layout [K-rows][BN bytes], XOR-swizzled at 16-byte granularity:

@@ -29,7 +29,9 @@
 //    K-rows x two 8-byte column halves; lane 8g+c receives column c of half g).
 // The 8-byte pieces 0..3 of a lane's 32 bytes thus hold K 16h+8p' + 32p''
 // (piece 2p''+p'), so pieces 0-1 of both lane groups cover K 0..31 and
-// pieces 2-3 cover K 32..63: one FP8 MFMA (K=64) takes all four, and the
+// pieces 2-3 cover K 32..63: one FP8 MFMA (K=64) takes all four -- the
+// instruction's own K order, so its 32-deep scale blocks (MODE_E8M0) are
+// K 0..31 and 32..63 of the slice -- and the
 // K=16 BF16 MFMA fed by piece p stays inside one 32-deep K block.
 #pragma once
 
@@ -64,6 +66,8 @@ enum Mode : int {
     MODE_EXACT = 1,  // E4M3 widened exactly to BF16, K=16 BF16 MFMAs
     MODE_BLOCK = 2,    // as MODE_EXACT, with a scale pair per 32x32 block and 32-deep K block
     MODE_BLOCK64 = 3,  // the same with 64x64 scale tiles and 64-deep K blocks (one per slice)
+    MODE_E8M0 = 4,     // native FP8 MFMA with a power-of-two (E8M0) scale per 32x32 tile of A and of B,
+                       // applied by the matrix core to each 32-deep K block
 };
 
 // FMT: operand formats, bit 0 set = A holds E5M2 codes, bit 1 = B (else E4M3).
@@ -74,10 +78,12 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     constexpr int KBD = MODE == MODE_BLOCK64 ? 64 : 32;  // K depth and edge of a scale tile
     constexpr int KB_PER_SLICE = BKP / KBD;             // scale blocks per 64-byte slice: 2 or 1
     static_assert(!BLOCKED || FMT == 0, "the block-scaled form takes E4M3 operands");
+    constexpr bool E8 = MODE == MODE_E8M0;
+    static_assert(!E8 || (FMT == 0 && KS == 1), "E8M0 tile scales: E4M3 operands, whole K blocks per wave");
     constexpr int FA = FMT & 1, FB = (FMT >> 1) & 1;
     using C = PipeCfg<BM, BN, WM, WN, KS, NB>;
     constexpr int TM = C::TM, TN = C::TN;
-    constexpr bool WIDEN = MODE != MODE_FAST;
+    constexpr bool WIDEN = MODE != MODE_FAST && !E8;
     static_assert(!BLOCKED || KS == 1, "block scales need whole K blocks per wave group");
     static_assert(MODE != MODE_BLOCK64 || (C::WTM % 64 == 0 && C::WTN % 64 == 0),
                   "a wave tile covers whole 64x64 scale tiles");
@@ -185,6 +191,11 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     // (pieces 2kb and 2kb+1 of the slice for 32-deep blocks, all four pieces
     // for 64-deep ones), folded into acc with its scale.
     v16f part[BLOCKED ? TM : 1][BLOCKED ? TN : 1];
+    // MODE_E8M0: this slice's scale operands, per lane: byte mi (ni) holds
+    // the exponent of A block mi (B block ni) for K block 2s + h (the scaled
+    // MFMA takes the exponent of 32-deep K block b of a row or column from
+    // lane group b), selected per MFMA by its op_sel field.
+    int e8a_lane = 0, e8b_lane = 0;
     auto mfma_one = [&](auto m_c, const Frags<TM, TN>& f) {
         constexpr int m = decltype(m_c)::value;
         if constexpr (MODE == MODE_EXACT) {
@@ -195,6 +206,9 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
             const v16f zero = {};
             constexpr bool first = MODE == MODE_BLOCK ? (c % 2 == 0) : (c == 0);  // first piece of its K block
             part[mi][ni] = mfma_32x32x16_bf16(bb[c & 1][ni], ab[c & 1][mi], first ? zero : part[mi][ni]);
+        } else if constexpr (E8) {
+            constexpr int mi = m / TN, ni = m % TN;
+            acc[mi][ni] = mfma_32x32x64_e4m3_scaled<ni, mi>(b_op(f, ni), a_op(f, mi), acc[mi][ni], e8b_lane, e8a_lane);
         } else {
             constexpr int mi = m / TN, ni = m % TN;
             acc[mi][ni] = mfma_32x32x64_f8<FB, FA>(b_op(f, ni), a_op(f, mi), acc[mi][ni]);
@@ -205,7 +219,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     // numbers of KBD-deep K blocks and KBD-wide column blocks.
     int sa_row[TM], sb_col[TN];
     const int64_t KBLK = K / KBD, NBLK = N / KBD;
-    if constexpr (BLOCKED) {
+    if constexpr (BLOCKED || E8) {
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
             sa_row[mi] = (int)min<int64_t>((t.m0 + wm * C::WTM + mi * 32) / KBD, t.M / KBD - 1);
@@ -213,6 +227,8 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
         for (int ni = 0; ni < TN; ++ni)
             sb_col[ni] = (int)min<int64_t>((t.n0 + wn * C::WTN + ni * 32) / KBD, NBLK - 1);
     }
+    // (The block modes are launched with K > 0 only: K == 0 has empty scale
+    // arrays, and its all-zero C is written by the launchers instead.)
     // Block modes' tile scales: read through the constant address space, so
     // they come in by scalar loads, counted by lgkmcnt rather than by the
     // vmcnt that tracks the stage loads, and one slice ahead, so the
@@ -229,6 +245,30 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
             for (int mi = 0; mi < TM; ++mi) sa_nx[r][mi] = *(cfloat*)(p.scale_a + sa_row[mi] * KBLK + k);
 #pragma unroll
             for (int ni = 0; ni < TN; ++ni) sb_nx[r][ni] = *(cfloat*)(p.scale_b + k * NBLK + sb_col[ni]);
+        }
+    };
+    // MODE_E8M0 tile exponents: the K-block-major byte arrays e8_a
+    // [K/32][pitch_a] and e8_b [K/32][pitch_b], each row padded to a
+    // multiple of 4 bytes, so that the TM (TN) consecutive row (column)
+    // tiles of a wave (TM, TN = 2 or 4, starting at a multiple of TM / TN)
+    // lie in one aligned 4-byte word per K block, at a byte shift fixed per
+    // wave.  Read through the constant address space (scalar loads, like the
+    // block scales above) one slice ahead.
+    typedef const __attribute__((address_space(4))) uint32_t cuint;
+    const uint32_t pitch_a = (uint32_t)((((t.M + 31) / 32) + 3) & ~3);
+    const uint32_t pitch_b = (uint32_t)((NBLK + 3) & ~3);
+    // first tile of the wave (clamped: a wave wholly past M or N stores
+    // nothing, but its reads must stay inside the arrays)
+    const uint32_t e8a_t0 = (uint32_t)min<int64_t>((t.m0 + wm * C::WTM) / 32, (t.M + 31) / 32 - 1);
+    const uint32_t e8b_t0 = (uint32_t)min<int64_t>((t.n0 + wn * C::WTN) / 32, NBLK - 1);
+    const uint32_t e8a_sh = 8 * (e8a_t0 & 3), e8b_sh = 8 * (e8b_t0 & 3);
+    uint32_t e8a_w[2], e8b_w[2];  // words of the next slice's K blocks 2s, 2s+1
+    auto load_slice_e8 = [&](int64_t sl) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const uint32_t k = (uint32_t)min<int64_t>(2 * sl + r, KBLK - 1);
+            e8a_w[r] = *(cuint*)(p.e8_a + (k * pitch_a + (e8a_t0 & ~3u)));
+            e8b_w[r] = *(cuint*)(p.e8_b + (k * pitch_b + (e8b_t0 & ~3u)));
         }
     };
     // acc += s_a * s_b * part for every accumulator block, with the scales
@@ -269,6 +309,7 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     static_assert(U % 2 == 0, "fragment register pairs and A-stage halves alternate");
     Frags<TM, TN> f0, f1;
     if constexpr (BLOCKED) load_slice_scales(0);
+    if constexpr (E8) load_slice_e8(0);
     loader.issue_a_half(-NB - 1);
 #pragma unroll
     for (int s = -NB; s < 0; ++s) loader.issue_slice(s);
@@ -299,6 +340,11 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
                     for (int ni = 0; ni < TN; ++ni) sb_cur[r][ni] = sb_nx[r][ni];
                 }
                 load_slice_scales(s + 1);
+            }
+            if constexpr (E8) {
+                e8a_lane = (int)((h ? e8a_w[1] : e8a_w[0]) >> e8a_sh);
+                e8b_lane = (int)((h ? e8b_w[1] : e8b_w[0]) >> e8b_sh);
+                load_slice_e8(s + 1);
             }
             // slice s+1: A stage (s+1)/2, slice (i+1)&1 of it; B buffer (i+1)%NB
             const lds_u8* abuf = lds + (((s + 1) >> 1) % C::NBUF_A) * C::A_STAGE;
@@ -454,9 +500,28 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     if constexpr (KS == 1) __syncthreads();
     using Store = TileStore<BF16, TM, TN>;
     lds_u8* scratch = lds + (KS > 1 ? C::RED : 0) + (wm * WN + wn) * Store::LDS_BYTES;
-    const float scale = BLOCKED ? 1.0f : p.scale_a[t.expert] * p.scale_b[t.expert];
+    const float scale = (BLOCKED || E8) ? 1.0f : p.scale_a[t.expert] * p.scale_b[t.expert];
     Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch,
                p.out_f16 != 0);
+}
+
+// Zero `bytes` bytes at p (16-byte aligned; a multiple of 2 bytes): a fill
+// kernel rather than a memset, so that a caller may capture it in a graph.
+__global__ void fill_zero_kernel(uint8_t* p, int64_t bytes) {
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16;
+    if (i + 16 <= bytes) {
+        *reinterpret_cast<v4i*>(p + i) = (v4i){0, 0, 0, 0};
+    } else {
+        for (int64_t j = i; j < bytes; ++j) p[j] = 0;
+    }
+}
+
+inline hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s) {
+    if (bytes <= 0) return hipSuccess;
+    const int64_t threads = (bytes + 15) / 16;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<uint8_t*>(p), bytes);
+    return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M, int MODE, bool SPLITK = false, int FMT = 0>
@@ -479,6 +544,8 @@ hipError_t launch_mode(const GemmProblem& g, hipStream_t s, int32_t splits = 1, 
                                : (int32_t)((g.M + (int64_t)g.experts * (BM - 1)) / BM);
     a.splits = SPLITK ? splits : 1;
     a.out_f16 = g.out_f16;
+    a.e8_a = g.e8_a;
+    a.e8_b = g.e8_b;
     a.ws = ws;
     a.counters = counters;
     const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * a.splits;

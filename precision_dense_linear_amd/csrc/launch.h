@@ -14,6 +14,10 @@ hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, floa
 // T x T tiles, T = 32 or 64
 hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, int T, uint8_t* q, float* tile_scales,
                                    hipStream_t s);
+// 32x32 tiles with E8M0 exponents (one byte per tile), stored
+// [rows/32][cols/32], or [cols/32][rows/32] when kmajor
+hipError_t launch_quantize_blocked_e8m0(const float* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* e8,
+                                        int kmajor, hipStream_t s);
 hipError_t launch_quantize_grouped(const float* x, int64_t rows, int64_t cols, const int32_t* offsets, int32_t groups,
                                    uint8_t* q, float* scales, float* amax, int fmt, hipStream_t s);
 
@@ -32,6 +36,8 @@ struct GemmProblem {
     int32_t fast_acc;  // 1: native FP8 MFMA accumulation; 0: exact products (BF16 MFMA)
     int32_t out_f16;   // 2-byte output is IEEE binary16
     int32_t fmt;       // operand formats: bit 0 set = A holds E5M2 codes, bit 1 = B (else E4M3)
+    const uint8_t* e8_a = nullptr;  // E8M0 tile exponents (block-scaled E8M0 GEMM only)
+    const uint8_t* e8_b = nullptr;
 };
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
 
@@ -40,6 +46,11 @@ hipError_t launch_gemm_fmt0(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_fmt1(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_fmt2(const GemmProblem& p, hipStream_t s);
 hipError_t launch_gemm_fmt3(const GemmProblem& p, hipStream_t s);
+
+// 32x32 tiles with E8M0 exponents e8_a [K/32][M/32], e8_b [K/32][N/32]
+// (M, N, K multiples of 32); out: 0 FP32, 1 BF16, 2 FP16
+hipError_t launch_gemm_blockscaled_e8m0(const uint8_t* A, const uint8_t* B, const uint8_t* e8_a, const uint8_t* e8_b,
+                                        void* C, int64_t M, int64_t N, int64_t K, int32_t out, hipStream_t s);
 
 // out: 0 FP32, 1 BF16, 2 FP16; block: edge of the scale tiles, 32 or 64
 hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,

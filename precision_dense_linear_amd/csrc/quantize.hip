@@ -114,11 +114,14 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const float* __restr
 // lanes of four floats (LPR lanes); load j of lane l covers tile row
 // (64/LPR) j + l/LPR, columns 4(l%LPR) .. +3, so each load instruction reads
 // whole 4T-byte row segments.  amax over the tile by a wave reduction, then
-// the codes (a T-byte run per row and instruction).
-template <int T>
+// the codes (a T-byte run per row and instruction).  E8: the tile's scale is
+// the power of two 2^e, e = floor(log2(amax)) - 8 clamped to [-127, 127]
+// (0 for an all-zero tile), stored as the byte e + 127 (E8M0) -- the OCP
+// microscaling conversion for E4M3 elements.
+template <int T, bool E8>
 __global__ void __launch_bounds__(kThreads) quantize_blocked_kernel(const float* __restrict__ x, int64_t rows,
                                                                     int64_t cols, uint8_t* __restrict__ q,
-                                                                    float* __restrict__ tile_scales) {
+                                                                    void* __restrict__ tile_scales, int kmajor) {
     constexpr int LPR = T / 4;        // lanes per tile row
     constexpr int RPI = 64 / LPR;     // tile rows per load instruction
     constexpr int NL = T / RPI;       // loads per lane
@@ -138,8 +141,24 @@ __global__ void __launch_bounds__(kThreads) quantize_blocked_kernel(const float*
 #pragma unroll
     for (int j = 0; j < NL; ++j) m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
     m = wave_max(m);
-    const float s = scale_from_amax(m);
-    if (lane == 0) tile_scales[tile] = s;
+    float s;
+    if constexpr (E8) {
+        int e = m == 0.0f ? 0 : __builtin_amdgcn_frexp_expf(m) - 1 - 8;  // m = f * 2^ex, f in [0.5, 1)
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        s = __builtin_amdgcn_ldexpf(1.0f, e);
+        // [rows/32][pitch(cols/32)], or [cols/32][pitch(rows/32)] (kmajor),
+        // pitch(n) = n rounded up to a multiple of 4; the last tile of each
+        // row also writes that row's padding bytes (127)
+        uint8_t* ex = reinterpret_cast<uint8_t*>(tile_scales);
+        const int64_t inner = kmajor ? rows / T : tiles_c;
+        const int64_t pitch = (inner + 3) & ~int64_t(3);
+        const int64_t outer_i = kmajor ? tj : ti, inner_i = kmajor ? ti : tj;
+        if (lane == 0) ex[outer_i * pitch + inner_i] = (uint8_t)(e + 127);
+        if (inner_i == inner - 1 && lane >= 1 && lane < 1 + pitch - inner) ex[outer_i * pitch + inner + lane - 1] = 127;
+    } else {
+        s = scale_from_amax(m);
+        if (lane == 0) reinterpret_cast<float*>(tile_scales)[tile] = s;
+    }
 #pragma unroll
     for (int j = 0; j < NL; ++j)
         *reinterpret_cast<uint32_t*>(q + (r + RPI * j) * cols + c) =
@@ -287,11 +306,21 @@ hipError_t launch_quantize_blocked(const float* x, int64_t rows, int64_t cols, i
     if (ntiles == 0) return hipSuccess;
     const int64_t blocks = (ntiles + kThreads / 64 - 1) / (kThreads / 64);
     if (T == 64)
-        hipLaunchKernelGGL(quantize_blocked_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, rows, cols, q,
-                           tile_scales);
+        hipLaunchKernelGGL((quantize_blocked_kernel<64, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, x, rows,
+                           cols, q, (void*)tile_scales, 0);
     else
-        hipLaunchKernelGGL(quantize_blocked_kernel<32>, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, rows, cols, q,
-                           tile_scales);
+        hipLaunchKernelGGL((quantize_blocked_kernel<32, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, x, rows,
+                           cols, q, (void*)tile_scales, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_blocked_e8m0(const float* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* e8,
+                                        int kmajor, hipStream_t s) {
+    const int64_t ntiles = (rows / 32) * (cols / 32);
+    if (ntiles == 0) return hipSuccess;
+    const int64_t blocks = (ntiles + kThreads / 64 - 1) / (kThreads / 64);
+    hipLaunchKernelGGL((quantize_blocked_kernel<32, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, x, rows,
+                       cols, q, (void*)e8, kmajor);
     return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
-              "fp8_quantize_grouped",
+              "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_grouped",
               "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
               "fp8_status_string", "fp8_last_error"):
         assert n in names
@@ -115,6 +115,14 @@ def test_quantize_validation():
         == P.FP8_ERR_INVALID_ARG
     assert L.fp8_quantize_blocked(FAKE, 48, 64, FAKE, FAKE, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
     assert L.fp8_quantize_blocked(FAKE, 64, 64, None, FAKE, None) == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize_blocked_e8m0(FAKE, 96, 48, 0, FAKE, FAKE, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert L.fp8_quantize_blocked_e8m0(FAKE, 64, 64, 2, FAKE, FAKE, None) == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize_blocked_e8m0(FAKE, 64, 64, 1, FAKE, None, None) == P.FP8_ERR_INVALID_ARG
+    f = L.fp8_gemm_blockscaled_e8m0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 48, 1, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 1 | P.FP8_ACC_FAST, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 2, None) == P.FP8_OK
     assert L.fp8_quantize_blocked64(FAKE, 96, 64, FAKE, FAKE, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
     assert L.fp8_quantize_blocked64(FAKE, 64, 64, None, FAKE, None) == P.FP8_ERR_INVALID_ARG
     assert L.fp8_quantize_blocked64(FAKE, 0, 64, FAKE, FAKE, None) == P.FP8_OK

@@ -25,6 +25,10 @@ paragraph -- grouped GEMM over experts):
 * ``quantize_blocked_e8m0`` / ``gemm_blockscaled_e8m0_rows`` -- 32x32 tile
                           scales as powers of two (OCP MX shared exponents,
                           E8M0 bytes).
+* ``prune_2of4`` / ``compress_2of4`` -- 2:4 magnitude pruning of the weights
+                          along K and the compressed (values, 2-bit
+                          positions) form the sparse matrix cores take; the
+                          GEMM itself is ``gemm_rows`` on the pruned codes.
 * ``e5m2_table``, ``quantize_*_fmt``, ``gemm_rows_fmt`` -- the same for OCP
                           E5M2 operands (scale = fl32(amax/57344)) and mixed
                           E4M3 x E5M2 pairs, summed exactly in 128-bit
@@ -113,6 +117,8 @@ def lib():
         L.orc_e8m0_exponent.argtypes = [f32]
         L.orc_quantize_blocked_e8m0.argtypes = [P, i64, i64, P, P]
         L.orc_gemm_blockscaled_e8m0_rows.argtypes = [P, P, P, P, i64, i64, P, i64, ctypes.c_int, P, P, P]
+        L.orc_prune_2of4.argtypes = [P, i64, i64, P]
+        L.orc_compress_2of4.argtypes = [P, i64, i64, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -502,3 +508,28 @@ def gemm_blockscaled_e8m0_rows(qa, qb, s_a, s_b, kind, rows=None):
     lib().orc_gemm_blockscaled_e8m0_rows(_p(qa), _p(qb), _p(s_a), _p(s_b), N, K, _p(rows), nr, kind, _p(out),
                                          _p(exact), _p(sab))
     return (out if kind == F32 else out.astype(np.uint16)), exact, sab
+
+
+# --------------------------------------------------------------------------
+# 2:4 structured sparsity of the weights ("FP8 GEMM in JAX with Triton for
+# Blackwell", opening section: sparsity support, ~2x at 50% sparsity)
+# --------------------------------------------------------------------------
+def prune_2of4(w: np.ndarray) -> np.ndarray:
+    """Keep the two largest-|w| entries (ties: lower k) of every group of 4 consecutive K of each column."""
+    w = _c(w, np.float32)
+    K, N = w.shape
+    assert K % 4 == 0
+    out = np.empty_like(w)
+    lib().orc_prune_2of4(_p(w), K, N, _p(out))
+    return out
+
+
+def compress_2of4(q: np.ndarray):
+    """2:4-sparse codes (K x N, K % 32 == 0) -> (vals uint8[K/2, N], idx uint32[K/32, N])."""
+    q = _c(q, np.uint8)
+    K, N = q.shape
+    assert K % 32 == 0
+    vals = np.empty((K // 2, N), np.uint8)
+    idx = np.empty((K // 32, N), np.uint32)
+    lib().orc_compress_2of4(_p(q), K, N, _p(vals), _p(idx))
+    return vals, idx

@@ -114,7 +114,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gemm8192",
                     choices=["gemm8192", "gemm1024", "gemm256", "llm16", "llm128", "llm4096", "blockscaled8192",
-                             "moe", "mixed8192", "blockscaled8192_64", "blockscaled8192_e8m0"])
+                             "moe", "mixed8192", "blockscaled8192_64", "blockscaled8192_e8m0", "sparse8192",
+                             "sparse_llm4096"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy twice (reference for the HBM byte counters)")
@@ -158,6 +159,18 @@ class Workload:
             a, b = W.llm_linear(self.M, self.N, self.K)
             self.desc = ("LLM linear layer M=%d N=%d K=%d, per-tensor FP8, BF16 out; activations N(0,1) with 1%% "
                          "outlier channels x20, weights N(0,0.02)" % (self.M, self.N, self.K))
+        elif name.startswith("sparse"):
+            self.kind = "sparse"
+            if name == "sparse8192":
+                self.M = self.N = self.K = 8192
+                a, b = W.pertensor_pair(8192, 8192, 8192, seed=0)
+                self.desc = ("per-tensor FP8 GEMM M=N=K=8192 with B 2:4-pruned along K on the sparse matrix cores, BF16 "
+                             "out; A, B FP32 N(0,1)")
+            else:
+                self.M, self.N, self.K = 4096, 28672, 8192
+                a, b = W.llm_linear(self.M, self.N, self.K)
+                self.desc = ("LLM linear layer M=4096 N=28672 K=8192 with the weights 2:4-pruned along K on the sparse "
+                             "matrix cores, BF16 out; activations N(0,1) with 1% outlier channels x20, weights N(0,0.02)")
         elif name == "blockscaled8192_e8m0":
             self.kind = "block_e8"
             self.M = self.N = self.K = 8192
@@ -185,8 +198,11 @@ class Workload:
         self.A, self.B = g(a), g(b)
         self.qa = torch.empty(a.shape, dtype=torch.uint8, device=dev)
         self.qb = torch.empty(b.shape, dtype=torch.uint8, device=dev)
+        if self.kind == "sparse":
+            self.qb = torch.empty((self.K // 2, self.N), dtype=torch.uint8, device=dev)
+            self.qi = torch.empty((self.K // 32, self.N), dtype=torch.int32, device=dev)
         self.C = torch.empty((self.M, self.N), dtype=self.out, device=dev)
-        if self.kind == "pertensor":
+        if self.kind in ("pertensor", "sparse"):
             self.sa, self.aa = (torch.empty(1, device=dev) for _ in range(2))
             self.sb, self.ab = (torch.empty(1, device=dev) for _ in range(2))
         elif self.kind == "block_e8":
@@ -206,6 +222,9 @@ class Workload:
         if self.kind == "pertensor":
             P.fp8_quantize(self.A, self.qa, self.sa, self.aa)
             (P.fp8_quantize_e5m2 if self.b_e5m2 else P.fp8_quantize)(self.B, self.qb, self.sb, self.ab)
+        elif self.kind == "sparse":
+            P.fp8_quantize(self.A, self.qa, self.sa, self.aa)
+            P.fp8_quantize_2of4(self.B, self.qb, self.qi, self.sb, self.ab)
         elif self.kind == "block_e8":
             P.fp8_quantize_blocked_e8m0(self.A, True, self.qa, self.sa)
             P.fp8_quantize_blocked_e8m0(self.B, False, self.qb, self.sb)
@@ -224,6 +243,8 @@ class Workload:
         if self.kind == "pertensor":
             P.fp8_gemm(qa, qb, self.sa, self.sb, self.out, C=self.C, fast=fast,
                        b_fmt="e5m2" if self.b_e5m2 else "e4m3")
+        elif self.kind == "sparse":
+            P.fp8_gemm_sparse24(qa, qb, self.qi, self.sa, self.sb, self.out, C=self.C)
         elif self.kind == "block_e8":
             P.fp8_gemm_blockscaled_e8m0(qa, qb, self.sa, self.sb, self.out, C=self.C)
         elif self.kind == "block":
@@ -245,6 +266,8 @@ class Workload:
         extra = (self.M // t) * (self.K // t) * 4 + (self.K // t) * (self.N // t) * 4 if self.kind == "block" else 0
         if self.kind == "block_e8":
             extra = (self.M // 32) * (self.K // 32) + (self.K // 32) * (self.N // 32)
+        if self.kind == "sparse":  # B: K/2 x N values + K/32 x N index words
+            return self.M * self.K + (self.K // 2) * self.N + (self.K // 32) * self.N * 4 + self.M * self.N * osz
         return self.M * self.K + self.K * self.N + self.M * self.N * osz + extra
 
 
@@ -331,7 +354,7 @@ def main():
 
     # the native-FP8-accumulation GEMM (FP8_ACC_FAST), timed the same way, outside the timed region
     fast = None
-    if w.kind not in ("block", "block_e8"):
+    if w.kind not in ("block", "block_e8", "sparse"):
         for _ in range(3):
             w.gemm(fast=True)
         fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -383,7 +406,18 @@ def main():
             rounds * ncopy, ncopy, (ncopy * per) >> 20,
             ", > 2x the 256 MB MALL: operands from HBM" if ncopy * per > 512e6 else ": small enough to stay cached")
         del cp
-    if mfma_bound and w.kind == "block_e8":
+    if mfma_bound and w.kind == "sparse":
+        # half of the products are structurally zero: the matrix cores execute
+        # M*N*K multiply-adds, priced against the dense FP8 rate (the sparse
+        # instructions reach twice the dense rate in K, i.e. the same rate of
+        # executed products)
+        peak = FP8_PEAK_TFLOPS
+        executed = gemm_tflops / 2
+        roof = {"bound": "mfma", "achieved": round(executed, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(executed / peak, 4), "traffic": measured_traffic(args.workload),
+                "peak_basis": "dense FP8 MFMA; achieved counts the executed (nonzero) products, 2*M*N*K/2; "
+                              "gemm_tflops counts the dense-equivalent 2*M*N*K"}
+    elif mfma_bound and w.kind == "block_e8":
         # power-of-two tile scales: the scaled FP8 matrix-core instructions
         peak = FP8_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak, "unit": "TFLOP/s",
@@ -406,6 +440,7 @@ def main():
         "block": ("gemm_kernel MODE_BLOCK64 (fp8_gemm_blockscaled, 64x64 tiles)" if getattr(w, "block", 32) == 64
                   else "gemm_kernel MODE_BLOCK (fp8_gemm_blockscaled)"),
         "block_e8": "gemm_kernel MODE_E8M0 (fp8_gemm_blockscaled_e8m0)",
+        "sparse": "gemm_kernel MODE_SPARSE (fp8_gemm_sparse24)",
         "moe": "gemm_kernel (fp8_grouped_gemm)"}[w.kind]
     roof["avg_kernel_us"] = round((avg_gemm_ms if mfma_bound else hbm_ms) * 1e3, 2)
     mhz = sclk.mean_mhz()

@@ -256,6 +256,42 @@ fp8_status fp8_gemm_blockscaled_e8m0(const uint8_t* A, const uint8_t* B, const u
                                      void* C, int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream);
 
 /*
+ * 2:4 structured sparsity of the weights ([P3] opening section: the matrix
+ * cores' sparsity support, about twice the efficiency at 50% weight
+ * sparsity).  fp8_quantize_2of4 prunes, quantizes and compresses a K x N
+ * weight matrix w (row-major, K % 32 == 0):
+ *   - in every group of 4 consecutive K of a column the two entries of
+ *     largest |w| are kept (ties: the lower k), the other two set to zero;
+ *   - the pruned matrix is quantized per tensor as by fp8_quantize (amax is
+ *     max |w|: the largest entry always survives);
+ *   - vals[(2g + j) * N + n] (K/2 x N bytes) = the j-th stored entry of
+ *     group g of column n, and idx[kb * N + n] (K/32 x N words) holds in
+ *     bits 2e .. 2e+1 the position (0..3) within its group of stored entry
+ *     e = 2 (g - 8 kb) + j of K block kb.  A group stores its entries whose
+ *     codes are nonzero (a kept value may round to zero), completed by its
+ *     lowest-k zero entries, in ascending k.
+ * w 16-byte aligned, idx 4-byte aligned; scale, amax one float each.
+ */
+fp8_status fp8_quantize_2of4(const float* w, int64_t K, int64_t N, uint8_t* vals, uint32_t* idx, float* scale,
+                             float* amax, void* stream);
+
+/*
+ * GEMM with a 2:4-sparse B on the sparse FP8 matrix cores:
+ *     C[m, n] = (scale_a * scale_b) * sum_k A[m, k] * B[k, n]
+ * with B given compressed as fp8_quantize_2of4 writes it (Bv: K/2 x N
+ * values, Bi: K/32 x N position words); every group of 4 of B holds at most
+ * 2 nonzero entries, so the matrix cores multiply only those, at twice the
+ * dense FP8 rate.  Accumulation as FP8_ACC_FAST (groups of products aligned
+ * to a 13-bit window, then FP32): |C - C_exact| <= (7 * 2^-13 + 2e-6) *
+ * sum_k |a*b| * scale_a * scale_b.  out_dtype: FP8_OUT_F32, _BF16 or _F16
+ * (no flags).  M, N, K >= 0; K % 32 == 0, N % 16 == 0, K <= 2^23; A, Bv, Bi,
+ * C 16-byte aligned.
+ */
+fp8_status fp8_gemm_sparse24(const uint8_t* A, const uint8_t* Bv, const uint32_t* Bi, const float* scale_a,
+                             const float* scale_b, void* C, int64_t M, int64_t N, int64_t K, int32_t out_dtype,
+                             void* stream);
+
+/*
  * MoE grouped FP8 GEMM ([P3] MoE paragraph: the GEMM extended to a grouped
  * GEMM over experts): for each expert e and each row r in
  * [offsets[e], offsets[e+1]):

@@ -17,6 +17,8 @@ Entry points (same names as the C ABI):
     fp8_gemm(A, B, scale_a, scale_b, out_dtype)
     fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype, block=32 | 64)
     fp8_gemm_blockscaled_e8m0(A, B, e_a, e_b, out_dtype)
+    fp8_quantize_2of4(w)                     -> (vals, idx, scale, amax)
+    fp8_gemm_sparse24(A, vals, idx, scale_a, scale_b, out_dtype)
     fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype)
 FP8 codes are passed as torch.uint8 (E4M3 unless a_fmt / b_fmt say "e5m2"),
 torch.float8_e4m3fn or torch.float8_e5m2 tensors; out_dtype is
@@ -39,7 +41,8 @@ FP8_A_E5M2, FP8_B_E5M2 = 0x200, 0x400  # operand formats (default E4M3)
 FP8_BLOCK64 = 0x800  # 64x64 scale tiles for the block-scaled GEMM
 
 SYMBOLS = ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
-           "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_grouped",
+           "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_2of4",
+           "fp8_gemm_sparse24", "fp8_quantize_grouped",
            "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
            "fp8_status_string", "fp8_last_error")
 
@@ -63,13 +66,16 @@ def _load():
     L.fp8_quantize_blocked64.argtypes = [P, i64, i64, P, P, P]
     L.fp8_quantize_blocked_e8m0.argtypes = [P, i64, i64, i32, P, P, P]
     L.fp8_gemm_blockscaled_e8m0.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
+    L.fp8_quantize_2of4.argtypes = [P, i64, i64, P, P, P, P, P]
+    L.fp8_gemm_sparse24.argtypes = [P, P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_quantize_grouped.argtypes = [P, i64, i64, P, i32, P, P, P, P]
     L.fp8_quantize_grouped_e5m2.argtypes = [P, i64, i64, P, i32, P, P, P, P]
     L.fp8_gemm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_gemm_blockscaled.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i64, i64, i64, i32, P]
     for f in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
-              "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_grouped",
+              "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_2of4",
+           "fp8_gemm_sparse24", "fp8_quantize_grouped",
               "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
         getattr(L, f).restype = st
     L.fp8_status_string.restype = ctypes.c_char_p
@@ -285,6 +291,42 @@ def fp8_gemm_blockscaled_e8m0(A, B, e_a, e_b, out_dtype=torch.bfloat16, C=None, 
         _check("fp8_gemm_blockscaled_e8m0", lib.fp8_gemm_blockscaled_e8m0(_ptr(A), _ptr(B), _ptr(e_a), _ptr(e_b),
                                                                           _ptr(C), M, N, K, code,
                                                                           _stream(A.device, stream)))
+    return C
+
+
+def fp8_quantize_2of4(w: torch.Tensor, vals=None, idx=None, scale=None, amax=None, stream=None):
+    """2:4-prune a K x N float32 weight matrix along K, quantize it per tensor (E4M3) and compress it;
+    returns (vals uint8[K/2, N], idx int32[K/32, N] position words, scale float32[1], amax float32[1])."""
+    _require(w.is_cuda and w.dtype == torch.float32 and w.is_contiguous() and w.dim() == 2,
+             "w must be a contiguous 2-D float32 GPU tensor")
+    K, N = w.shape
+    dev = w.device
+    vals = torch.empty((K // 2, N), dtype=torch.uint8, device=dev) if vals is None else vals
+    idx = torch.empty((K // 32, N), dtype=torch.int32, device=dev) if idx is None else idx
+    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
+    amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else amax
+    with torch.cuda.device(dev):
+        _check("fp8_quantize_2of4", lib.fp8_quantize_2of4(_ptr(w), K, N, _ptr(vals), _ptr(idx), _ptr(scale),
+                                                          _ptr(amax), _stream(dev, stream)))
+    return vals, idx, scale, amax
+
+
+def fp8_gemm_sparse24(A, vals, idx, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=None):
+    """C = scale_a*scale_b * A @ B with E4M3 A (M x K) and a 2:4-sparse B given compressed
+    (vals [K/2, N], idx [K/32, N]) on the sparse FP8 matrix cores."""
+    _require(_fmt_flag(A, None, 1) == 0, "E4M3 operands only")
+    A = _codes(A)
+    vals = vals.view(torch.uint8) if vals.dtype == torch.float8_e4m3fn else vals
+    M, K = A.shape
+    N = vals.shape[1]
+    _require(vals.shape[0] * 2 == K and tuple(idx.shape) == (K // 32, N), "A is %s but vals %s, idx %s" % (
+        tuple(A.shape), tuple(vals.shape), tuple(idx.shape)))
+    code = _out_code(out_dtype)
+    C = _out_tensor(C, (M, N), code, A.device)
+    with torch.cuda.device(A.device):
+        _check("fp8_gemm_sparse24", lib.fp8_gemm_sparse24(_ptr(A), _ptr(vals), _ptr(idx), _ptr(scale_a),
+                                                          _ptr(scale_b), _ptr(C), M, N, K, code,
+                                                          _stream(A.device, stream)))
     return C
 
 

@@ -208,6 +208,35 @@ fp8_status fp8_gemm_blockscaled_e8m0(const uint8_t* A, const uint8_t* B, const u
         "fp8_gemm_blockscaled_e8m0");
 }
 
+fp8_status fp8_quantize_2of4(const float* w, int64_t K, int64_t N, uint8_t* vals, uint32_t* idx, float* scale,
+                             float* amax, void* stream) {
+    if (K < 0 || N < 0) return fail(FP8_ERR_INVALID_ARG, "negative size");
+    if (!scale || !amax || (K * N > 0 && (!w || !vals || !idx))) return fail(FP8_ERR_INVALID_ARG, "null pointer argument");
+    if (K % 32) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld must be a multiple of 32", (long long)K);
+    if (!aligned16(w) || ((uintptr_t)idx & 3)) return fail(FP8_ERR_INVALID_ARG, "w must be 16-byte and idx 4-byte aligned");
+    if (scale == amax) return fail(FP8_ERR_INVALID_ARG, "scale and amax must be distinct");
+    if (K > kMaxK || N > kMaxN) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K or N too large");
+    return from_hip(fp8k::launch_quantize_2of4(w, K, N, vals, idx, scale, amax, (hipStream_t)stream),
+                    "fp8_quantize_2of4");
+}
+
+fp8_status fp8_gemm_sparse24(const uint8_t* A, const uint8_t* Bv, const uint32_t* Bi, const float* scale_a,
+                             const float* scale_b, void* C, int64_t M, int64_t N, int64_t K, int32_t out_dtype,
+                             void* stream) {
+    fp8_status st = check_gemm_common(A, Bv, C, M, N, K, out_dtype, 0);
+    if (st != FP8_OK) return st;
+    if (!scale_a || !scale_b) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
+    if (!Bi && K * N > 0) return fail(FP8_ERR_INVALID_ARG, "null index pointer");
+    if (!aligned16(Bi)) return fail(FP8_ERR_INVALID_ARG, "the index words must be 16-byte aligned");
+    if (K % 32 || N % 16)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld must be a multiple of 32 and N=%lld of 16", (long long)K,
+                    (long long)N);
+    if (M == 0 || N == 0) return ok();
+    return from_hip(fp8k::launch_gemm_sparse24(A, Bv, Bi, scale_a, scale_b, C, M, N, K, out_dtype & 0xFF,
+                                               (hipStream_t)stream),
+                    "fp8_gemm_sparse24");
+}
+
 fp8_status fp8_grouped_gemm(const uint8_t* A, const uint8_t* B, const int32_t* offsets, int32_t experts,
                             const float* scale_a, const float* scale_b, void* C, int64_t T, int64_t N, int64_t K,
                             int32_t out_dtype, void* stream) {

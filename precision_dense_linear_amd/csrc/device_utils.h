@@ -54,6 +54,18 @@ __device__ __forceinline__ v16f mfma_32x32x64_e4m3_scaled(v8i a, v8i b, v16f c, 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, BYTE0, e8_src0, BYTE1, e8_src1);
 }
 
+// D = A(32x64, 2:4 sparse along K) * B(64x32) + C, E4M3 operands, FP32
+// accumulate (v_smfmac_f32_32x32x64_fp8_fp8).  A is given compressed: lane
+// l (h = l/32) holds for row l%32 the 16 kept values of instruction K
+// 32h .. 32h+31 in K order (two per group of 4), and idx bits 2e .. 2e+1
+// give the position (0..3) of kept value e within its group.  B as for the
+// dense instruction (bytes 0-15: K 16h..16h+15, 16-31: K 32+16h..), the
+// accumulator layout too.  (Both layouts were checked on the GPU against
+// the exact product of small-integer operands.)
+__device__ __forceinline__ v16f smfmac_32x32x64_e4m3(v4i a_sparse, v8i b, v16f c, int idx) {
+    return __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(a_sparse, b, c, idx, 0, 0);
+}
+
 // D = A(32x16) * B(16x32) + C in BF16 with FP32 accumulate
 // (v_mfma_f32_32x32x16_bf16).  Lane l holds A row l%32 / B column l%32, K
 // elements 8*(l/32) .. +7; accumulator layout as for the 32x32x64 form.

@@ -32,6 +32,7 @@ struct GemmArgs {
     int32_t out_f16;  // 2-byte output is IEEE binary16 rather than BF16
     const uint8_t* e8_a;  // E8M0 tile exponents of A [K/32][M/32] (MODE_E8M0 only)
     const uint8_t* e8_b;  // E8M0 tile exponents of B [K/32][N/32]
+    const uint32_t* sp_idx;  // 2:4-sparse B: 2-bit positions [K/32][N] (B then holds the values [K/2][N])
 };
 
 // B stage layout [K-rows][BN bytes], XOR-swizzled at 16-byte granularity:
@@ -135,7 +136,7 @@ constexpr int BKA = 128;  // bytes of K per wave group per A stage
 
 __device__ __forceinline__ int swz_a128(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-template <int BM, int BN, int WM, int WN, int KS, int NB_>
+template <int BM, int BN, int WM, int WN, int KS, int NB_, bool SP = false>
 struct PipeCfg {
     static constexpr int NBUF_B = NB_;               // B stage buffers: NB-1 slices of look-ahead
     static constexpr int NBUF_A = (NB_ + 2) / 2;     // A stage buffers (two slices each)
@@ -143,7 +144,13 @@ struct PipeCfg {
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
     static constexpr int A_STAGE = KS * BM * BKA;
-    static constexpr int B_STAGE = KS * BKP * BN;
+    // B stage: the slice's B rows; for a 2:4-sparse B (SP) its 32 compressed
+    // value rows, then the index words of its two 32-deep K blocks for the
+    // tile's BN columns ([2][BN] x 4 bytes), padded to whole loads per wave.
+    static constexpr int B_VAL = KS * (SP ? BKP / 2 : BKP) * BN;
+    static constexpr int B_IDX = SP ? 2 * BN * 4 : 0;
+    static constexpr int B_STAGE = (B_VAL + B_IDX + 1024 * NW - 1) / (1024 * NW) * (1024 * NW);
+    static constexpr int NB_VAL = B_VAL / 1024, NB_IDX = B_IDX / 1024;  // 1 KiB load slots of values, of index
     static constexpr int B_BASE = NBUF_A * A_STAGE;  // LDS offset of the B stages
     static constexpr int NA = A_STAGE / 1024 / NW;   // loads per wave per A stage
     static constexpr int NB = B_STAGE / 1024 / NW;   // loads per wave per B stage
@@ -157,6 +164,7 @@ struct PipeCfg {
     static_assert(NB_ >= 4 && NB_ % 2 == 0, "B buffers: even, at least 4");
     static_assert((NB_ - 1) * LPS <= 63, "in-flight loads must fit the vmcnt counter");
     static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(!SP || (KS == 1 && B_IDX % 1024 == 0), "sparse B: one wave group, whole index loads");
 };
 
 // One wave-wide global->LDS load, written as inline assembly: M0 holds the
@@ -197,26 +205,37 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
 // fragments are in registers by slice s; A stage a is issued from slice
 // 2a-NB-1 into the buffer of stage a-NBUF_A, last read in slice
 // 2(a-NBUF_A) <= 2a-NB-2 because 2*NBUF_A >= NB+2.
-template <int BM, int BN, int WM, int WN, int KS, int NB>
+template <int BM, int BN, int WM, int WN, int KS, int NB, bool SP = false>
 struct PipeLoader {
-    using C = PipeCfg<BM, BN, WM, WN, KS, NB>;
+    using C = PipeCfg<BM, BN, WM, WN, KS, NB, SP>;
     uint32_t a_off[C::NA], a_kk[C::NA], b_off[C::NB];
+    bool b_idx[C::NB];  // SP: load slot i of this wave fetches index words (else values)
     const uint8_t* a_base;
     const uint8_t* b_base;
-    int64_t a_bytes, b_bytes, K, N;
+    const uint8_t* i_base;  // SP: index words of the tile's first column
+    int64_t a_bytes, b_bytes, i_bytes, K, N;
     uint32_t lds_wave;  // LDS byte address of this wave's first 1 KiB slot
 
     // Loads K bytes [k_begin, k_end) of the tile's A rows and B columns (the
     // whole K unless split-K gives this workgroup a part).
     __device__ __forceinline__ PipeLoader(const TileSlice& t, int64_t N_, int64_t K_, int64_t k_begin, int64_t k_end,
-                                          int wave, int lane, uint32_t lds_base) {
+                                          int wave, int lane, uint32_t lds_base, const uint32_t* sp_idx = nullptr) {
         K = k_end - k_begin;  // K range this loader covers (A rows keep the full stride K_)
         N = N_;
         const int64_t rows_here = t.M - t.m0;
         a_base = t.A + t.m0 * K_ + k_begin;
         a_bytes = rows_here * K_ - k_begin;
-        b_base = t.B + t.n0 + k_begin * N;
-        b_bytes = K * N - t.n0;
+        if constexpr (SP) {  // values [K/2][N], index words [K/32][N] (whole K: no split-K here)
+            b_base = t.B + t.n0;
+            b_bytes = (K / 2) * N - t.n0;
+            i_base = reinterpret_cast<const uint8_t*>(sp_idx) + t.n0 * 4;
+            i_bytes = ((K + 31) / 32) * N * 4 - t.n0 * 4;
+        } else {
+            b_base = t.B + t.n0 + k_begin * N;
+            b_bytes = K * N - t.n0;
+            i_base = nullptr;
+            i_bytes = 0;
+        }
         lds_wave = lds_base + wave * 1024;
 #pragma unroll
         for (int i = 0; i < C::NA; ++i) {
@@ -230,19 +249,37 @@ struct PipeLoader {
         }
 #pragma unroll
         for (int i = 0; i < C::NB; ++i) {
-            const int slot = (i * C::NW + wave) * 64 + lane;
-            const int sub = slot / (BKP * BN / 16);
-            const int s2 = slot % (BKP * BN / 16);
-            const int r = s2 / (BN / 16);
-            const int c = swz_b<BN>(r, s2 % (BN / 16));
-            b_off[i] = (t.n0 + c * 16 < N) ? (uint32_t)((sub * BKA + r) * N + c * 16) : OOB;
+            if constexpr (SP) {
+                const int ld = i * C::NW + wave;  // 1 KiB slot of the stage
+                b_idx[i] = ld >= C::NB_VAL;
+                if (ld < C::NB_VAL) {  // value rows, swizzled as B
+                    const int s2 = ld * 64 + lane;
+                    const int r = s2 / (BN / 16);
+                    const int c = swz_b<BN>(r, s2 % (BN / 16));
+                    b_off[i] = (t.n0 + c * 16 < N) ? (uint32_t)(r * N + c * 16) : OOB;
+                } else if (ld < C::NB_VAL + C::NB_IDX) {  // index words: K block o / (4 BN), 4 columns per lane
+                    const int o = (ld - C::NB_VAL) * 1024 + lane * 16;
+                    const int kb = o / (BN * 4), w = o % (BN * 4);
+                    b_off[i] = (t.n0 + w / 4 < N) ? (uint32_t)(kb * N * 4 + w) : OOB;
+                } else {
+                    b_off[i] = OOB;  // padding of the stage
+                }
+            } else {
+                const int slot = (i * C::NW + wave) * 64 + lane;
+                const int sub = slot / (BKP * BN / 16);
+                const int s2 = slot % (BKP * BN / 16);
+                const int r = s2 / (BN / 16);
+                const int c = swz_b<BN>(r, s2 % (BN / 16));
+                b_off[i] = (t.n0 + c * 16 < N) ? (uint32_t)((sub * BKA + r) * N + c * 16) : OOB;
+                b_idx[i] = false;
+            }
         }
     }
 
     // The loads of slice s (see above): resources and LDS destinations.  Past
     // the end of K the resources are empty, so every load reads zero.
     struct Stage {
-        __amdgpu_buffer_rsrc_t ra, rb;
+        __amdgpu_buffer_rsrc_t ra, rb, ri;
         int64_t krem;
         uint32_t dst_a, dst_b;
     };
@@ -253,7 +290,13 @@ struct PipeLoader {
         const int64_t kb0 = (int64_t)(jb >> 1) * (KS * BKA) + (jb & 1) * BKP;
         const int64_t ka0 = (int64_t)ja * (KS * BKA);
         g.ra = make_rsrc(a_base + ka0, clamp_records(a_bytes - ka0));
-        g.rb = make_rsrc(b_base + kb0 * N, clamp_records(b_bytes - kb0 * N));
+        if constexpr (SP) {  // compressed rows kb0/2 .., index row kb0/32 ..
+            g.rb = make_rsrc(b_base + (kb0 / 2) * N, clamp_records(b_bytes - (kb0 / 2) * N));
+            g.ri = make_rsrc(i_base + (kb0 / 32) * N * 4, clamp_records(i_bytes - (kb0 / 32) * N * 4));
+        } else {
+            g.rb = make_rsrc(b_base + kb0 * N, clamp_records(b_bytes - kb0 * N));
+            g.ri = g.rb;
+        }
         g.krem = K - ka0;
         g.dst_a = __builtin_amdgcn_readfirstlane(lds_wave + (uint32_t)(ja % C::NBUF_A) * C::A_STAGE);
         g.dst_b = __builtin_amdgcn_readfirstlane(lds_wave + C::B_BASE + (uint32_t)(jb % NB) * C::B_STAGE);
@@ -263,7 +306,7 @@ struct PipeLoader {
     // first, then the A stage's loads [half * NA/2, half * NA/2 + NA/2).
     __device__ __forceinline__ void issue_one(const Stage& g, int r, int half) const {
         if (r < C::NB) {
-            dma16(g.rb, g.dst_b + r * C::NW * 1024, b_off[r]);
+            dma16((SP && b_idx[r]) ? g.ri : g.rb, g.dst_b + r * C::NW * 1024, b_off[r]);
         } else {
             const int i = half * (C::NA / 2) + (r - C::NB);
             dma16(g.ra, g.dst_a + i * C::NW * 1024, (int64_t)a_kk[i] < g.krem ? a_off[i] : OOB);

@@ -49,6 +49,7 @@ template <int TM, int TN>
 struct Frags {
     v4i a[TM][2];
     v2i b[TN][4];
+    int idx[TN];  // MODE_SPARSE: the 2-bit positions of the B block's kept values
 };
 
 // Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
@@ -68,6 +69,7 @@ enum Mode : int {
     MODE_BLOCK64 = 3,  // the same with 64x64 scale tiles and 64-deep K blocks (one per slice)
     MODE_E8M0 = 4,     // native FP8 MFMA with a power-of-two (E8M0) scale per 32x32 tile of A and of B,
                        // applied by the matrix core to each 32-deep K block
+    MODE_SPARSE = 5,   // 2:4-sparse B (compressed values + 2-bit positions) on the sparse FP8 MFMA
 };
 
 // FMT: operand formats, bit 0 set = A holds E5M2 codes, bit 1 = B (else E4M3).
@@ -79,11 +81,13 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     constexpr int KB_PER_SLICE = BKP / KBD;             // scale blocks per 64-byte slice: 2 or 1
     static_assert(!BLOCKED || FMT == 0, "the block-scaled form takes E4M3 operands");
     constexpr bool E8 = MODE == MODE_E8M0;
+    constexpr bool SP = MODE == MODE_SPARSE;
+    static_assert(!SP || (FMT == 0 && KS == 1 && !SPLITK), "sparse B: E4M3, one wave group, no split-K");
     static_assert(!E8 || (FMT == 0 && KS == 1), "E8M0 tile scales: E4M3 operands, whole K blocks per wave");
     constexpr int FA = FMT & 1, FB = (FMT >> 1) & 1;
-    using C = PipeCfg<BM, BN, WM, WN, KS, NB>;
+    using C = PipeCfg<BM, BN, WM, WN, KS, NB, SP>;
     constexpr int TM = C::TM, TN = C::TN;
-    constexpr bool WIDEN = MODE != MODE_FAST && !E8;
+    constexpr bool WIDEN = MODE != MODE_FAST && !E8 && !SP;
     static_assert(!BLOCKED || KS == 1, "block scales need whole K blocks per wave group");
     static_assert(MODE != MODE_BLOCK64 || (C::WTM % 64 == 0 && C::WTN % 64 == 0),
                   "a wave tile covers whole 64x64 scale tiles");
@@ -110,8 +114,8 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     // slices per wave group: whole A stages
     const int nsteps = 2 * (int)((k_end - k_begin + kstep - 1) / kstep);
     lds_u8* lds = (lds_u8*)smem;
-    using Loader = PipeLoader<BM, BN, WM, WN, KS, NB>;
-    const Loader loader(t, N, K, k_begin, k_end, wave, lane, (uint32_t)(uintptr_t)lds);
+    using Loader = PipeLoader<BM, BN, WM, WN, KS, NB, SP>;
+    const Loader loader(t, N, K, k_begin, k_end, wave, lane, (uint32_t)(uintptr_t)lds, p.sp_idx);
 
     v16f acc[TM][TN];
 #pragma unroll
@@ -142,23 +146,34 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
         const int col = wn * C::WTN + ni * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 #pragma unroll
         for (int tq = 0; tq < 4; ++tq) {
-            const int kr = 16 * h + 8 * (tq & 1) + 32 * (tq >> 1) + ((lane & 15) >> 1);
+            // SP: pieces 0, 1 are compressed rows 16h .. 16h+15 (the kept values of K 32h .. 32h+31)
+            const int kr = SP ? 16 * h + 8 * (tq & 1) + ((lane & 15) >> 1)
+                              : 16 * h + 8 * (tq & 1) + 32 * (tq >> 1) + ((lane & 15) >> 1);
             b_off[ni][tq] = C::B_BASE + ks * BKP * BN + kr * BN + swz_b<BN>(kr, col >> 4) * 16 + (col & 15);
         }
     }
+    // SP: the index word of K block 2s + h for this lane's column of B block ni
+    int idx_off[TN];
+#pragma unroll
+    for (int ni = 0; ni < TN; ++ni) idx_off[ni] = C::B_BASE + C::B_VAL + h * BN * 4 + (wn * C::WTN + ni * 32 + (lane & 31)) * 4;
 
     // A slice's LDS reads in a fixed order: q < 2*TM reads chunk q%2 of A
-    // block q/2, the rest read piece (q-2TM)%4 of B block (q-2TM)/4.  `abuf`
-    // is the LDS address of the slice's A stage; U (slice within the A stage)
-    // and BB (B stage buffer) are compile-time.
-    constexpr int RD = 2 * TM + 4 * TN;
+    // block q/2, the rest read piece (q-2TM)%PB of B block (q-2TM)/PB (PB = 4
+    // pieces, or 2 of compressed values in MODE_SPARSE, followed there by the
+    // TN index words).  `abuf` is the LDS address of the slice's A stage; U
+    // (slice within the A stage) and BB (B stage buffer) are compile-time.
+    constexpr int PB = SP ? 2 : 4;
+    constexpr int RD = 2 * TM + PB * TN + (SP ? TN : 0);
     auto read_one = [&](auto q_c, auto u_c, auto bb_c, const lds_u8* abuf, Frags<TM, TN>& f) {
         constexpr int q = decltype(q_c)::value, u = decltype(u_c)::value, bb = decltype(bb_c)::value;
         if constexpr (q < 2 * TM) {
             f.a[q / 2][q % 2] = lds_read16(abuf + a_off[u][q / 2][q % 2]);
-        } else {
+        } else if constexpr (q < 2 * TM + PB * TN) {
             constexpr int qb = q - 2 * TM;
-            f.b[qb / 4][qb % 4] = lds_read_tr8(lds + bb * C::B_STAGE + b_off[qb / 4][qb % 4]);
+            f.b[qb / PB][qb % PB] = lds_read_tr8(lds + bb * C::B_STAGE + b_off[qb / PB][qb % PB]);
+        } else {
+            constexpr int qi = q - 2 * TM - PB * TN;
+            f.idx[qi] = *(const __attribute__((address_space(3))) int*)(lds + bb * C::B_STAGE + idx_off[qi]);
         }
     };
     auto a_op = [](const Frags<TM, TN>& f, int mi) {
@@ -168,6 +183,9 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     auto b_op = [](const Frags<TM, TN>& f, int ni) {
         return (v8i){f.b[ni][0][0], f.b[ni][0][1], f.b[ni][1][0], f.b[ni][1][1],
                      f.b[ni][2][0], f.b[ni][2][1], f.b[ni][3][0], f.b[ni][3][1]};
+    };
+    auto b_sparse_op = [](const Frags<TM, TN>& f, int ni) {  // 16 compressed values: K 32h .. 32h+31
+        return (v4i){f.b[ni][0][0], f.b[ni][0][1], f.b[ni][1][0], f.b[ni][1][1]};
     };
 
     // The slice's matrix instructions in a fixed order.  Fast: one K=64 FP8
@@ -206,6 +224,9 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
             const v16f zero = {};
             constexpr bool first = MODE == MODE_BLOCK ? (c % 2 == 0) : (c == 0);  // first piece of its K block
             part[mi][ni] = mfma_32x32x16_bf16(bb[c & 1][ni], ab[c & 1][mi], first ? zero : part[mi][ni]);
+        } else if constexpr (SP) {
+            constexpr int mi = m / TN, ni = m % TN;
+            acc[mi][ni] = smfmac_32x32x64_e4m3(b_sparse_op(f, ni), a_op(f, mi), acc[mi][ni], f.idx[ni]);
         } else if constexpr (E8) {
             constexpr int mi = m / TN, ni = m % TN;
             acc[mi][ni] = mfma_32x32x64_e4m3_scaled<ni, mi>(b_op(f, ni), a_op(f, mi), acc[mi][ni], e8b_lane, e8a_lane);
@@ -546,6 +567,7 @@ hipError_t launch_mode(const GemmProblem& g, hipStream_t s, int32_t splits = 1, 
     a.out_f16 = g.out_f16;
     a.e8_a = g.e8_a;
     a.e8_b = g.e8_b;
+    a.sp_idx = g.sp_idx;
     a.ws = ws;
     a.counters = counters;
     const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * a.splits;

@@ -38,6 +38,7 @@ struct GemmProblem {
     int32_t fmt;       // operand formats: bit 0 set = A holds E5M2 codes, bit 1 = B (else E4M3)
     const uint8_t* e8_a = nullptr;  // E8M0 tile exponents (block-scaled E8M0 GEMM only)
     const uint8_t* e8_b = nullptr;
+    const uint32_t* sp_idx = nullptr;  // 2:4-sparse B (B then holds the compressed values)
 };
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
 
@@ -51,6 +52,14 @@ hipError_t launch_gemm_fmt3(const GemmProblem& p, hipStream_t s);
 // (M, N, K multiples of 32); out: 0 FP32, 1 BF16, 2 FP16
 hipError_t launch_gemm_blockscaled_e8m0(const uint8_t* A, const uint8_t* B, const uint8_t* e8_a, const uint8_t* e8_b,
                                         void* C, int64_t M, int64_t N, int64_t K, int32_t out, hipStream_t s);
+
+// 2:4-sparse B: values [K/2][N], positions idx [K/32][N] (K % 32 == 0)
+hipError_t launch_gemm_sparse24(const uint8_t* A, const uint8_t* Bv, const uint32_t* Bi, const float* scale_a,
+                                const float* scale_b, void* C, int64_t M, int64_t N, int64_t K, int32_t out,
+                                hipStream_t s);
+// prune (2 of every 4 along K), quantize per tensor and compress a K x N weight matrix
+hipError_t launch_quantize_2of4(const float* w, int64_t K, int64_t N, uint8_t* vals, uint32_t* idx, float* scale,
+                                float* amax, hipStream_t s);
 
 // out: 0 FP32, 1 BF16, 2 FP16; block: edge of the scale tiles, 32 or 64
 hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,

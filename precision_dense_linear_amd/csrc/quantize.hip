@@ -280,7 +280,74 @@ __global__ void __launch_bounds__(kThreads) quantize_grouped_kernel(const float*
     }
 }
 
+// 2:4 pruning, per-tensor E4M3 quantization and compression of a K x N
+// weight matrix (K % 32 == 0), the scale taken from *amax (the largest |w|
+// always survives the pruning).  One wave per 64 columns and one 32-deep K
+// block; lane = column, so each load and store instruction touches one
+// 64-column run of a row.  Per group of 4 along K: keep the two largest |w|
+// (the first maximum on ties), quantize them (the other two become code
+// 0x00), then store the group's two entries that are nonzero codes (a kept
+// value may round to zero), completed by its lowest-k zero entries, in
+// ascending k, with their 2-bit positions.
+__global__ void __launch_bounds__(kThreads) quantize_2of4_kernel(const float* __restrict__ w, int64_t K, int64_t N,
+                                                                 const float* __restrict__ amax,
+                                                                 uint8_t* __restrict__ vals, uint32_t* __restrict__ idx,
+                                                                 float* scale_out) {
+    const float s = scale_from_amax(*amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+    const int lane = threadIdx.x & 63;
+    const int64_t wv = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int64_t colblocks = (N + 63) / 64;
+    const int64_t kb = wv / colblocks, n = (wv % colblocks) * 64 + lane;
+    if (kb >= K / 32 || n >= N) return;
+    uint32_t word = 0;
+#pragma unroll
+    for (int gg = 0; gg < 8; ++gg) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = w[(kb * 32 + gg * 4 + q) * N + n];
+        int best = 0;
+#pragma unroll
+        for (int q = 1; q < 4; ++q) if (fabsf(v[q]) > fabsf(v[best])) best = q;
+        int second = best == 0 ? 1 : 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) if (q != best && fabsf(v[q]) > fabsf(v[second])) second = q;
+        uint8_t c[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c[q] = (q == best || q == second) ? e4m3_sat(__fdiv_rn(v[q], s)) : (uint8_t)0;
+        int pos[2] = {0, 0}, np = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (np < 2 && (c[q] & 0x7F) != 0) pos[np++] = q;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (np < 2 && (c[q] & 0x7F) == 0 && !(np == 1 && pos[0] == q)) pos[np++] = q;
+        if (pos[0] > pos[1]) { const int t = pos[0]; pos[0] = pos[1]; pos[1] = t; }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            vals[(kb * 16 + gg * 2 + j) * N + n] = c[pos[j]];
+            word |= (uint32_t)pos[j] << (2 * (2 * gg + j));
+        }
+    }
+    idx[kb * N + n] = word;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_2of4(const float* w, int64_t K, int64_t N, uint8_t* vals, uint32_t* idx, float* scale,
+                                float* amax, hipStream_t s) {
+    hipLaunchKernelGGL(fill_f32, dim3(1), dim3(64), 0, s, amax, 1, 0.0f);
+    const int64_t n = K * N;
+    const int64_t nchunks = ((n >> 2) + CHUNK4 - 1) / CHUNK4;
+    const int64_t cpb = nchunks < 2048 ? 1 : (nchunks + 2047) / 2048;
+    const int64_t blocks = nchunks < 1 ? 1 : (nchunks + cpb - 1) / cpb;
+    if (n > 0) hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, w, n, cpb, amax);
+    const int64_t waves = (K / 32) * ((N + 63) / 64);
+    const int64_t qblocks = waves < 1 ? 1 : (waves + kThreads / 64 - 1) / (kThreads / 64);
+    hipLaunchKernelGGL(quantize_2of4_kernel, dim3((unsigned)qblocks), dim3(kThreads), 0, s, w, K, N,
+                       (const float*)amax, vals, idx, scale);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, float* scale, float* amax, int fmt,
                                      hipStream_t s) {

@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
-              "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_grouped",
+              "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_2of4", "fp8_gemm_sparse24",
+              "fp8_quantize_grouped",
               "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
               "fp8_status_string", "fp8_last_error"):
         assert n in names
@@ -123,6 +124,18 @@ def test_quantize_validation():
     assert f(FAKE, FAKE, None, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 1 | P.FP8_ACC_FAST, None) == P.FP8_ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 2, None) == P.FP8_OK
+    assert L.fp8_quantize_2of4(FAKE, 48, 64, FAKE, FAKE, FAKE, ctypes.c_void_p(0x200000), None) \
+        == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert L.fp8_quantize_2of4(FAKE, 64, 64, None, FAKE, FAKE, ctypes.c_void_p(0x200000), None) \
+        == P.FP8_ERR_INVALID_ARG
+    assert L.fp8_quantize_2of4(FAKE, 64, 64, FAKE, FAKE, FAKE, FAKE, None) == P.FP8_ERR_INVALID_ARG   # scale is amax
+    f = L.fp8_gemm_sparse24
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 48, 1, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 40, 64, 1, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert f(FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE_ODD, FAKE, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 1 | P.FP8_ACC_FAST, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 2, None) == P.FP8_OK
     assert L.fp8_quantize_blocked64(FAKE, 96, 64, FAKE, FAKE, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
     assert L.fp8_quantize_blocked64(FAKE, 64, 64, None, FAKE, None) == P.FP8_ERR_INVALID_ARG
     assert L.fp8_quantize_blocked64(FAKE, 0, 64, FAKE, FAKE, None) == P.FP8_OK

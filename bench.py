@@ -18,6 +18,8 @@ Printed (rank 0, one JSON line):
                  one B would be served from the MALL, not HBM)
   sclk        -- the GPU clock sampled during the timed region, and the
                  GEMM's fraction of the MFMA peak at that clock
+  vendor_same_box -- context only: hipBLASLt's FP8 and BF16 GEMMs (through
+                 torch) on the same codes and shape, timed the same way
   cpu_baseline-- the CPU oracle timed on a bounded sample of the same step
 Other workloads (--workload) serve profiling of the other shape classes.
 """
@@ -117,6 +119,7 @@ def parse():
                              "moe", "mixed8192", "blockscaled8192_64", "blockscaled8192_e8m0", "sparse8192",
                              "sparse_llm4096"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-vendor", action="store_true", help="skip timing the vendor GEMM library for comparison")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy twice (reference for the HBM byte counters)")
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
@@ -308,6 +311,42 @@ def cpu_baseline(w: Workload, rows: int):
                                                                     t_step)}
 
 
+def vendor_reference(w: Workload):
+    """Context, not part of the step: the vendor GEMM library (hipBLASLt, via
+    torch) on the same shape and device, timed like the GEMM above -- its FP8
+    GEMM on the same E4M3 codes (B handed over in the column-major layout it
+    takes) and its BF16 GEMM on the codes widened to BF16."""
+    torch = w.torch
+    if w.kind != "pertensor" or w.b_e5m2 or w.out != torch.bfloat16:
+        return None
+    out = {"library": "hipBLASLt via torch._scaled_mm (FP8) and torch.matmul (BF16)"}
+    a8 = w.qa.view(torch.float8_e4m3fn)
+    bt8 = w.qb.t().contiguous().view(torch.float8_e4m3fn)  # N x K, K contiguous
+    sa, sb = w.sa.reshape(()), w.sb.reshape(())
+
+    def timed(fn, n=20):
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for s_, e_ in ev:
+            s_.record()
+            fn()
+            e_.record()
+        torch.cuda.synchronize()
+        us = float(np.median([s_.elapsed_time(e_) for s_, e_ in ev])) * 1e3
+        return {"median_us": round(us, 2), "tflops": round(w.flops / (us * 1e-6) / 1e12, 2)}
+
+    try:
+        out["fp8"] = timed(lambda: torch._scaled_mm(a8, bt8.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16))
+    except Exception as e:  # library without FP8 support on this device
+        out["fp8"] = {"error": repr(e)[:200]}
+    a16 = a8.to(torch.bfloat16)
+    bt16 = bt8.to(torch.bfloat16)
+    out["bf16"] = timed(lambda: a16 @ bt16.t())
+    del a16, bt16, bt8
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -443,6 +482,7 @@ def main():
         "sparse": "gemm_kernel MODE_SPARSE (fp8_gemm_sparse24)",
         "moe": "gemm_kernel (fp8_grouped_gemm)"}[w.kind]
     roof["avg_kernel_us"] = round((avg_gemm_ms if mfma_bound else hbm_ms) * 1e3, 2)
+    vendor = None if args.no_vendor else vendor_reference(w)
     mhz = sclk.mean_mhz()
     sclk_out = None
     if mhz is not None:
@@ -474,6 +514,7 @@ def main():
         "roofline": roof,
         "sclk": sclk_out,
         "fp8_acc_fast": fast,
+        "vendor_same_box": vendor,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

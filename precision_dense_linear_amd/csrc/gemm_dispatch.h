@@ -44,13 +44,20 @@ hipError_t launch_cfg_splitk(const GemmProblem& g, hipStream_t s, int32_t splits
 //    also splits K across workgroups (measured on M = 16/32, N = 8192,
 //    K = 8192 with B out of HBM: 36.5 -> 26 us);
 //  * M <= 1024: 128 x 128 tiles, 4 waves of 64 x 64 per K half, the K range
-//    split over two wave groups (more loads in flight per tile);
+//    split over two wave groups (more loads in flight per tile) -- unless a
+//    plain GEMM has so few of them that they would fill under half of the
+//    CUs: then the 32 x 64 class above (measured, kernel time, exact mode:
+//    1024^3 11.8 -> 8.6 us, 512 x 2048 x 4096 27.0 -> 18.6 us, 1024 x 1024
+//    x 8192 47.6 -> 32.8 us; at 128 and more such tiles, e.g. 1024 x 2048 x
+//    1024, the 128 x 128 class stays faster);
 //  * larger M: 256 x 256 tiles, 4 waves of 128 x 128 -- MFMA bound.
 template <int FMT>
 hipError_t launch_gemm_t(const GemmProblem& g, hipStream_t s) {
     const bool plain = g.experts == 0;
     const int64_t rows_per_problem = plain ? g.M : (g.M + g.experts - 1) / g.experts;
-    if (rows_per_problem <= 64) {
+    // split_slots() is twice the CU count
+    const bool few_mid_tiles = plain && tiles_of(g.M, g.N, 128, 128) * 4 < split_slots();
+    if (rows_per_problem <= 64 || (rows_per_problem <= 1024 && few_mid_tiles)) {
         const int sp = plain ? choose_splits(tiles_of(g.M, g.N, 32, 64), g.K, 2) : 1;
         if (sp > 1) return launch_cfg_splitk<FMT, 32, 64, 1, 2, 2, 4, 8>(g, s, sp);
         return launch_cfg<FMT, 32, 64, 1, 2, 2, 4, 8>(g, s);

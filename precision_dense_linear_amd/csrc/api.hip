@@ -39,6 +39,10 @@ fp8_status check_gemm_common(const void* A, const void* B, const void* C, int64_
                              int32_t out_dtype, int32_t allowed_flags) {
     if (M < 0 || N < 0 || K < 0) return fail(FP8_ERR_INVALID_ARG, "negative size (M=%lld N=%lld K=%lld)",
                                              (long long)M, (long long)N, (long long)K);
+    // size limits first: past them M * K, K * N or M * N could overflow below
+    if (K > kMaxK) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld exceeds 2^23", (long long)K);
+    if (N > kMaxN) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "N=%lld exceeds 2^20", (long long)N);
+    if (M > (int64_t(1) << 31) - 1) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "M=%lld exceeds 2^31-1", (long long)M);
     // an operand with no elements may be null
     if ((!A && M * K > 0) || (!B && K * N > 0) || (!C && M * N > 0))
         return fail(FP8_ERR_INVALID_ARG, "null matrix pointer");
@@ -52,9 +56,6 @@ fp8_status check_gemm_common(const void* A, const void* B, const void* C, int64_
                     "FP8_B_E5M2)",
                     out_dtype);
     if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return fail(FP8_ERR_INVALID_ARG, "A, B and C must be 16-byte aligned");
-    if (K > kMaxK) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld exceeds 2^23", (long long)K);
-    if (N > kMaxN) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "N=%lld exceeds 2^20", (long long)N);
-    if (M > (int64_t(1) << 31) - 1) return fail(FP8_ERR_UNSUPPORTED_SHAPE, "M=%lld exceeds 2^31-1", (long long)M);
     return FP8_OK;
 }
 

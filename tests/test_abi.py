@@ -69,6 +69,9 @@ def gemm(A=FAKE, B=FAKE, sa=FAKE, sb=FAKE, C=FAKE, M=64, N=64, K=64, out=1):
     (dict(K=40), P.FP8_ERR_UNSUPPORTED_SHAPE),
     (dict(N=40), P.FP8_ERR_UNSUPPORTED_SHAPE),
     (dict(K=(1 << 23) + 16), P.FP8_ERR_UNSUPPORTED_SHAPE),
+    (dict(A=None, M=1 << 40, K=1 << 40), P.FP8_ERR_UNSUPPORTED_SHAPE),  # limits come before M*K is formed
+    (dict(M=1 << 31), P.FP8_ERR_UNSUPPORTED_SHAPE),
+    (dict(N=1 << 21), P.FP8_ERR_UNSUPPORTED_SHAPE),
     (dict(M=0), P.FP8_OK),            # empty: nothing to enqueue
     (dict(N=0), P.FP8_OK),
 ])

@@ -171,7 +171,10 @@ struct PipeCfg {
 // wave's LDS destination, lane l's 16 bytes land at M0 + 16*l.  The compiler
 // does not see these as LDS writes, so it neither serialises later LDS reads
 // behind them nor counts them; the kernel waits for them explicitly with
-// s_waitcnt vmcnt(n), n = loads issued after the stage it needs.
+// s_waitcnt vmcnt(n), n = loads issued after the stage it needs.  M0 is
+// listed as clobbered, which the compiler does not promise to honour for a
+// reserved register; that is safe only while no other code in these kernels
+// keeps a value in M0 (their gfx950 assembly has no other M0 access).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :

@@ -20,6 +20,7 @@ Printed (rank 0, one JSON line):
                  GEMM's fraction of the MFMA peak at that clock
   vendor_same_box -- context only: hipBLASLt's FP8 and BF16 GEMMs (through
                  torch) on the same codes and shape, timed the same way
+                 (BF16 with B as an N x K weight, and with row-major B)
   cpu_baseline-- the CPU oracle timed on a bounded sample of the same step
 Other workloads (--workload) serve profiling of the other shape classes.
 """
@@ -315,11 +316,12 @@ def vendor_reference(w: Workload):
     """Context, not part of the step: the vendor GEMM library (hipBLASLt, via
     torch) on the same shape and device, timed like the GEMM above -- its FP8
     GEMM on the same E4M3 codes (B handed over in the column-major layout it
-    takes) and its BF16 GEMM on the codes widened to BF16."""
+    takes) and its BF16 GEMM on the codes widened to BF16, with B as an N x K
+    weight (its fastest layout) and as the row-major K x N matrix."""
     torch = w.torch
     if w.kind != "pertensor" or w.b_e5m2 or w.out != torch.bfloat16:
         return None
-    out = {"library": "hipBLASLt via torch._scaled_mm (FP8) and torch.matmul (BF16)"}
+    out = {"library": "hipBLASLt via torch._scaled_mm (FP8), torch.nn.functional.linear and torch.matmul (BF16)"}
     a8 = w.qa.view(torch.float8_e4m3fn)
     bt8 = w.qb.t().contiguous().view(torch.float8_e4m3fn)  # N x K, K contiguous
     sa, sb = w.sa.reshape(()), w.sb.reshape(())
@@ -340,10 +342,15 @@ def vendor_reference(w: Workload):
         out["fp8"] = timed(lambda: torch._scaled_mm(a8, bt8.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16))
     except Exception as e:  # library without FP8 support on this device
         out["fp8"] = {"error": repr(e)[:200]}
+    # BF16 in the layout that library is fastest with (B as an N x K weight,
+    # nn.Linear's convention; a plain 2-D product), and with row-major B
     a16 = a8.to(torch.bfloat16)
     bt16 = bt8.to(torch.bfloat16)
-    out["bf16"] = timed(lambda: a16 @ bt16.t())
-    del a16, bt16, bt8
+    out["bf16"] = timed(lambda: torch.nn.functional.linear(a16, bt16))
+    del bt16
+    b16 = w.qb.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    out["bf16_b_row_major"] = timed(lambda: torch.matmul(a16, b16))
+    del a16, b16, bt8
     return out
 
 

@@ -125,7 +125,7 @@ def parse():
                     help="only run a plain 1 GiB device copy twice (reference for the HBM byte counters)")
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="keep warming up at least this long so clocks have settled")
-    ap.add_argument("--cpu-rows", type=int, default=768, help="rows of A in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of A in the oracle's timed sample (about 10 s of CPU work at 8192^3)")
     return ap.parse_args()
 
 

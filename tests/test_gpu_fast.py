@@ -52,7 +52,7 @@ def check_fast(C, exact, sab_scaled, what):
 
 
 @pytest.mark.parametrize("shape,out", [((256, 256, 256), torch.float32), ((1024, 1024, 1024), torch.bfloat16)])
-def test_fast_configs_within_bound(shape, out):
+def test_fast_workloads_within_bound(shape, out):
     M, N, K = shape
     a, b = W.pertensor_pair(M, N, K, seed=0)
     qa, sa, _ = P.fp8_quantize(gpu(a))

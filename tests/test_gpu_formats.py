@@ -62,7 +62,7 @@ def test_quantize_e5m2_ragged_lengths(n):
     quantize_e5m2_and_check(x, "n=%d" % n)
 
 
-def test_quantize_e5m2_config_operands_and_weights():
+def test_quantize_e5m2_operands_and_weights():
     a, b = W.pertensor_pair(8192, 8192, 8192, seed=1)
     quantize_e5m2_and_check(a, "A 8192^2")
     _, w = W.llm_linear(16, 8192, 8192)

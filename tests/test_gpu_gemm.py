@@ -55,12 +55,12 @@ def pertensor_end_to_end(a, b, kind, rows=None, what=""):
 
 
 # ------------------------------------------------------------------ configurations
-def test_config_256_f32():
+def test_pertensor_256_f32():
     a, b = W.pertensor_pair(256, 256, 256, seed=0)
     pertensor_end_to_end(a, b, F32, what="256^3 FP32")
 
 
-def test_config_1024_bf16_and_determinism():
+def test_pertensor_1024_bf16_and_determinism():
     a, b = W.pertensor_pair(1024, 1024, 1024, seed=0)
     C1 = pertensor_end_to_end(a, b, BF16, what="1024^3 BF16")
     C2 = pertensor_end_to_end(a, b, BF16, what="1024^3 BF16 again")
@@ -68,7 +68,7 @@ def test_config_1024_bf16_and_determinism():
 
 
 @pytest.mark.parametrize("M,N", [(16, 8192), (128, 28672), (4096, 28672)])
-def test_config_llm_linear_bf16(M, N):
+def test_llm_linear_k8192_bf16(M, N):
     a, w = W.llm_linear(M, N, 8192)
     rows = None if M <= 16 else sample_rows(M, 12, M)
     pertensor_end_to_end(a, w, BF16, rows=rows, what="LLM M=%d N=%d K=8192" % (M, N))
@@ -223,7 +223,7 @@ def test_blockscaled_zero_tiles():
     blockscaled_end_to_end(a, b, BF16, what="block-scaled with zero tiles")
 
 
-def test_blockscaled_config4_sampled():
+def test_blockscaled_8192_tile_factors_sampled():
     a, b = W.blockscaled_pair(8192, 8192, 8192, seed=0)
     blockscaled_end_to_end(a, b, BF16, rows=sample_rows(8192, 10, 2), what="block-scaled 8192^3 BF16")
 
@@ -274,7 +274,7 @@ def test_grouped_single_expert_equals_gemm():
     assert torch.equal(C, C2)
 
 
-def test_grouped_config5_moe_sampled():
+def test_grouped_moe_8_experts_16384_tokens_sampled():
     x, w, off = W.moe()
     rows = np.concatenate([sample_rows(int(off[e + 1] - off[e]), 3, e) + off[e] for e in range(8)])
     grouped_end_to_end(x, w, off, BF16, rows=np.unique(rows), what="MoE 8 experts Zipf(1.2) T=16384")

@@ -58,7 +58,7 @@ def test_quantize_ties_and_saturation():
 
 
 @pytest.mark.parametrize("shape", [(256, 256), (1024, 1024), (8192, 8192)])
-def test_quantize_config_operands(shape):
+def test_quantize_pertensor_operands(shape):
     a, b = W.pertensor_pair(shape[0], shape[1], shape[0], seed=1)
     quantize_and_check(a, "A%s" % (shape,))
 
@@ -93,7 +93,7 @@ def test_convert_sweep_all_fp32_patterns():
         print("sweep chunk %#010x done" % c0, flush=True)
 
 
-def test_quantize_blocked_config4_full():
+def test_quantize_blocked_8192_tile_factors_full():
     a, b = W.blockscaled_pair(8192, 8192, 8192)
     for name, x in (("A", a), ("B", b)):
         q, ts = P.fp8_quantize_blocked(gpu(x))

@@ -204,14 +204,19 @@ fp8_status fp8_quantize_grouped_e5m2(const float* x, int64_t rows, int64_t cols,
  * M, N, K >= 0; K % 16 == 0 and N % 16 == 0 (16-byte rows), K <= 2^23,
  * else FP8_ERR_UNSUPPORTED_SHAPE.  A, B, C 16-byte aligned.  M == 0 or
  * N == 0 enqueues nothing; K == 0 writes zeros.
- * Split-K: when M <= 64 and the output has too few 32 x 64 tiles to fill
- * the GPU, the K range is split over up to 8 workgroups per tile; their
+ * Split-K: when the 32 x 64 tile class runs (M <= 64, or M <= 1024 with
+ * fewer 128 x 128 tiles than half the GPU's CUs) and the output has too few
+ * 32 x 64 tiles to fill the GPU, the K range is split over up to 8
+ * workgroups per tile; their
  * FP32 partial sums meet in the stream's workspace and are added in a fixed
  * order, so results stay deterministic run to run (they may differ in the
  * last bits from an unsplit sum).  The first such call on a stream
  * allocates the workspace (hipMalloc may synchronise the device; a call
  * under stream capture must have been preceded by one outside it); calls
  * on different streams use different workspaces and may run concurrently.
+ * A graph captured from such a call keeps the capture stream's workspace:
+ * replaying it while split-K calls run on that stream, or replaying two
+ * such graphs at once, races.
  */
 fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
                     int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream);

@@ -160,3 +160,19 @@ def test_binding_refuses_wrong_operand_dtype():
     assert P._fmt_flag(torch.zeros(4, dtype=torch.float8_e5m2), None, P.FP8_B_E5M2) == P.FP8_B_E5M2
     assert P._fmt_flag(torch.zeros(4, dtype=torch.uint8), "e5m2", P.FP8_A_E5M2) == P.FP8_A_E5M2
     assert P._fmt_flag(torch.zeros(4, dtype=torch.uint8), None, P.FP8_A_E5M2) == 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """The binding has no fallback: a package directory without the built
+    library refuses to import (nothing runs on the CPU in its place)."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "precision_dense_linear_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(P.__file__), "__init__.py"), pkg / "__init__.py")
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "try:\n    import precision_dense_linear_amd\nexcept ImportError as e:\n    print('IMPORT-ERROR', e)\n"
+            "else:\n    print('IMPORTED', precision_dense_linear_amd.__file__)\n") % str(tmp_path)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300).stdout
+    assert "IMPORT-ERROR" in out and "not built" in out, out

@@ -274,6 +274,21 @@ def test_grouped_single_expert_equals_gemm():
     assert torch.equal(C, C2)
 
 
+@pytest.mark.parametrize("kind", [F32, BF16])
+def test_grouped_large_experts_ragged_ends(kind):
+    """Over 1024 rows per expert on average (the 256 x 256 tile class): expert
+    ends at every kind of position inside a 256-row tile (0, under 128, 127,
+    128 and over 128 rows past the last whole tile), an empty expert, a
+    ragged N; every output compared."""
+    rng = np.random.default_rng(31)
+    counts = np.array([1100, 0, 1280, 1919, 1408, 550])  # remainders 76, -, 0, 127, 128, 38
+    off = np.concatenate([[0], np.cumsum(counts)])
+    T, K, N, E = int(off[-1]), 320, 272, len(counts)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    w = (rng.standard_normal((E, K, N)) * 0.02).astype(np.float32)
+    grouped_end_to_end(x, w, off, kind, what="grouped, large experts, ragged ends")
+
+
 def test_grouped_moe_8_experts_16384_tokens_sampled():
     x, w, off = W.moe()
     rows = np.concatenate([sample_rows(int(off[e + 1] - off[e]), 3, e) + off[e] for e in range(8)])

@@ -207,10 +207,9 @@ fp8_status fp8_quantize_grouped_e5m2(const float* x, int64_t rows, int64_t cols,
  * Split-K: when the 32 x 64 tile class runs (M <= 64, or M <= 1024 with
  * fewer 128 x 128 tiles than half the GPU's CUs) and the output has too few
  * 32 x 64 tiles to fill the GPU, the K range is split over up to 8
- * workgroups per tile; their
- * FP32 partial sums meet in the stream's workspace and are added in a fixed
- * order, so results stay deterministic run to run (they may differ in the
- * last bits from an unsplit sum).  The first such call on a stream
+ * workgroups per tile; their FP32 partial sums meet in the stream's
+ * workspace and are added in a fixed order, so results stay deterministic
+ * run to run (they may differ in the last bits from an unsplit sum).  The first such call on a stream
  * allocates the workspace (hipMalloc may synchronise the device; a call
  * under stream capture must have been preceded by one outside it); calls
  * on different streams use different workspaces and may run concurrently.

@@ -14,7 +14,8 @@ Entry points (same names as the C ABI):
     fp8_quantize_blocked_e8m0(x, k_major)    -> (q, tile_exps uint8)
     fp8_quantize_grouped(x, offsets)         -> (q, scales, amax)
     fp8_quantize_grouped_e5m2(x, offsets)    -> (q, scales, amax)
-    fp8_gemm(A, B, scale_a, scale_b, out_dtype)
+    fp8_gemm(A, B, scale_a, scale_b, out_dtype)   (fp8_gemm_ws with workspace=)
+    gemm_workspace(device)                   -> zeroed split-K workspace (torch.uint8)
     fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype, block=32 | 64)
     fp8_gemm_blockscaled_e8m0(A, B, e_a, e_b, out_dtype)
     fp8_quantize_2of4(w)                     -> (vals, idx, scale, amax)
@@ -39,11 +40,13 @@ FP8_OUT_F32, FP8_OUT_BF16, FP8_OUT_F16 = 0, 1, 2
 FP8_ACC_FAST = 0x100  # native FP8 matrix-core accumulation (see include/fp8gemm.h)
 FP8_A_E5M2, FP8_B_E5M2 = 0x200, 0x400  # operand formats (default E4M3)
 FP8_BLOCK64 = 0x800  # 64x64 scale tiles for the block-scaled GEMM
+FP8_GEMM_WS_TILE_BYTES = 8196  # split-K workspace bytes per split tile (32 x 64 FP32 partials + counter)
+FP8_GEMM_WORKSPACE_BYTES = 512 * FP8_GEMM_WS_TILE_BYTES
 
 SYMBOLS = ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
            "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_2of4",
            "fp8_gemm_sparse24", "fp8_quantize_grouped",
-           "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
+           "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_ws", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
            "fp8_status_string", "fp8_last_error")
 
 
@@ -71,12 +74,13 @@ def _load():
     L.fp8_quantize_grouped.argtypes = [P, i64, i64, P, i32, P, P, P, P]
     L.fp8_quantize_grouped_e5m2.argtypes = [P, i64, i64, P, i32, P, P, P, P]
     L.fp8_gemm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
+    L.fp8_gemm_ws.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P, i64, P]
     L.fp8_gemm_blockscaled.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i64, i64, i64, i32, P]
     for f in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
               "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_2of4",
            "fp8_gemm_sparse24", "fp8_quantize_grouped",
-              "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
+              "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_ws", "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
         getattr(L, f).restype = st
     L.fp8_status_string.restype = ctypes.c_char_p
     L.fp8_status_string.argtypes = [i32]
@@ -239,12 +243,21 @@ def _out_tensor(C, shape, code, dev):
     return torch.empty(shape, dtype=dt, device=dev)
 
 
+def gemm_workspace(device=None, nbytes: int = FP8_GEMM_WORKSPACE_BYTES) -> torch.Tensor:
+    """A zero-filled split-K workspace for fp8_gemm(..., workspace=...)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+
+
 def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=None, fast=False, a_fmt=None,
-             b_fmt=None):
+             b_fmt=None, workspace=None):
     """C = scale_a*scale_b * A @ B with FP8 A (M x K) and B (K x N), FP32 accumulation.
 
     fast=True selects the native FP8 matrix-core accumulation (FP8_ACC_FAST);
-    a_fmt / b_fmt ("e4m3" or "e5m2") give the operand formats of uint8 codes."""
+    a_fmt / b_fmt ("e4m3" or "e5m2") give the operand formats of uint8 codes.
+    workspace (a zeroed uint8 GPU tensor, e.g. gemm_workspace()) calls
+    fp8_gemm_ws, which may split K across workgroups for outputs too small to
+    fill the GPU; calls sharing a workspace must be ordered (one stream)."""
     flags = _fmt_flag(A, a_fmt, FP8_A_E5M2) | _fmt_flag(B, b_fmt, FP8_B_E5M2) | (FP8_ACC_FAST if fast else 0)
     A, B = _codes(A), _codes(B)
     M, K = A.shape
@@ -253,8 +266,15 @@ def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=No
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
     with torch.cuda.device(A.device):
-        _check("fp8_gemm", lib.fp8_gemm(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N, K,
-                                        code | flags, _stream(A.device, stream)))
+        if workspace is None:
+            _check("fp8_gemm", lib.fp8_gemm(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N, K,
+                                            code | flags, _stream(A.device, stream)))
+        else:
+            _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous GPU tensor")
+            _check("fp8_gemm_ws", lib.fp8_gemm_ws(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N,
+                                                  K, code | flags, _ptr(workspace),
+                                                  workspace.numel() * workspace.element_size(),
+                                                  _stream(A.device, stream)))
     return C
 
 

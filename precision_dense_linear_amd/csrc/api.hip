@@ -34,6 +34,10 @@ fp8_status from_hip(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxK = int64_t(1) << 23;  // 256 rows x K stays below 2^31 bytes per tile
 constexpr int64_t kMaxN = int64_t(1) << 20;  // 256 K-rows x N stays below 2^31 bytes per step
+// Split-K workspace: per split tile, the FP32 partial sums of a 32 x 64 tile
+// and a 4-byte arrival counter (FP8_GEMM_WS_TILE_BYTES in all).
+constexpr int64_t kSplitTileFloatBytes = 32 * 64 * 4;
+static_assert(kSplitTileFloatBytes + 4 == FP8_GEMM_WS_TILE_BYTES, "workspace tile size");
 
 fp8_status check_gemm_common(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
                              int32_t out_dtype, int32_t allowed_flags) {
@@ -162,8 +166,11 @@ fp8_status fp8_quantize_grouped_e5m2(const float* x, int64_t rows, int64_t cols,
     return quantize_grouped(x, rows, cols, offsets, groups, q, scales, amax, 1, stream, "fp8_quantize_grouped_e5m2");
 }
 
-fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
-                    int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
+// The per-tensor GEMM with an optional split-K workspace (ws_tiles split
+// tiles: FP32 partial sums first, then one arrival counter per split tile).
+fp8_status gemm_pertensor(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
+                          int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* ws, int64_t ws_tiles,
+                          void* stream, const char* what) {
     fp8_status st = check_gemm_common(A, B, C, M, N, K, out_dtype, FP8_ACC_FAST | FP8_A_E5M2 | FP8_B_E5M2);
     if (st != FP8_OK) return st;
     if (!scale_a || !scale_b) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
@@ -172,7 +179,27 @@ fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, co
     if (M == 0 || N == 0) return ok();
     fp8k::GemmProblem g{A, B, C, scale_a, scale_b, nullptr, 0, M, N, K, 0, 0, 0, 0};
     decode_out(out_dtype, g);
-    return from_hip(fp8k::launch_gemm(g, (hipStream_t)stream), "fp8_gemm");
+    if (ws && ws_tiles > 0) {
+        g.ws = static_cast<float*>(ws);
+        g.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + ws_tiles * kSplitTileFloatBytes);
+        g.ws_tiles = ws_tiles;
+    }
+    return from_hip(fp8k::launch_gemm(g, (hipStream_t)stream), what);
+}
+
+fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
+                    int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
+    return gemm_pertensor(A, B, scale_a, scale_b, C, M, N, K, out_dtype, nullptr, 0, stream, "fp8_gemm");
+}
+
+fp8_status fp8_gemm_ws(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
+                       int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
+    if (workspace_bytes < 0) return fail(FP8_ERR_INVALID_ARG, "negative workspace_bytes=%lld", (long long)workspace_bytes);
+    if (!workspace && workspace_bytes > 0) return fail(FP8_ERR_INVALID_ARG, "null workspace with workspace_bytes > 0");
+    if (!aligned16(workspace)) return fail(FP8_ERR_INVALID_ARG, "the workspace must be 16-byte aligned");
+    return gemm_pertensor(A, B, scale_a, scale_b, C, M, N, K, out_dtype, workspace,
+                          workspace_bytes / FP8_GEMM_WS_TILE_BYTES, stream, "fp8_gemm_ws");
 }
 
 fp8_status fp8_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,

@@ -331,8 +331,9 @@ struct PipeLoader {
     }
 };
 
-// Epilogue: store the wave's TM x TN accumulator blocks, multiplied by
-// `scale`.  The kernels issue each MFMA with the B fragment as the first
+// Epilogue: store the wave's TM x TN accumulator blocks, each sum
+// multiplied by `sa` and then by `sb` (two roundings; the product sa * sb
+// itself could fall below the normal binary32 range where C does not).  The kernels issue each MFMA with the B fragment as the first
 // operand, so accumulator block (mi, ni) holds C^T: element r of lane l is
 // row 32mi + (l & 31), column 32ni + 8(r >> 2) + 4(l >> 5) + (r & 3) of the
 // wave tile -- four consecutive columns of one row per r/4 group.  Those go
@@ -353,7 +354,7 @@ struct TileStore {
 
     __device__ static __forceinline__ int swz(int row, int ch) { return ch ^ (row & (CHUNKS - 1)); }
 
-    __device__ static __forceinline__ void run(void* C, const v16f (&acc)[TM][TN], float scale, int64_t m_base,
+    __device__ static __forceinline__ void run(void* C, const v16f (&acc)[TM][TN], float sa, float sb, int64_t m_base,
                                                int64_t n_base, int64_t M, int64_t N, int64_t c_row0, int lane,
                                                lds_u8* scratch, bool f16) {
         const bool full = (m_base + 32 * TM <= M) && (n_base + 32 * TN <= N);
@@ -373,21 +374,20 @@ struct TileStore {
                         const v16f& a = acc[p0 + mi][ni];
                         const int cb = (ni * 32 + 8 * q + 4 * (lane >> 5)) * OSZ;  // byte column in the row
                         lds_u8* dst = scratch + row * ROWB + swz(row, cb >> 4) * 16 + (cb & 15);
+                        const float c0 = (a[4 * q] * sa) * sb, c1 = (a[4 * q + 1] * sa) * sb;
+                        const float c2 = (a[4 * q + 2] * sa) * sb, c3 = (a[4 * q + 3] * sa) * sb;
                         if constexpr (BF16) {
                             if (f16) {
                                 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-                                const v4h v = {(_Float16)(a[4 * q] * scale), (_Float16)(a[4 * q + 1] * scale),
-                                               (_Float16)(a[4 * q + 2] * scale), (_Float16)(a[4 * q + 3] * scale)};
+                                const v4h v = {(_Float16)c0, (_Float16)c1, (_Float16)c2, (_Float16)c3};
                                 *(__attribute__((address_space(3))) v4h*)dst = v;
                             } else {
                                 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
-                                const v4bf v = {(__bf16)(a[4 * q] * scale), (__bf16)(a[4 * q + 1] * scale),
-                                                (__bf16)(a[4 * q + 2] * scale), (__bf16)(a[4 * q + 3] * scale)};
+                                const v4bf v = {(__bf16)c0, (__bf16)c1, (__bf16)c2, (__bf16)c3};
                                 *(__attribute__((address_space(3))) v4bf*)dst = v;
                             }
                         } else {
-                            const v4f v = {a[4 * q] * scale, a[4 * q + 1] * scale, a[4 * q + 2] * scale,
-                                           a[4 * q + 3] * scale};
+                            const v4f v = {c0, c1, c2, c3};
                             *(__attribute__((address_space(3))) v4f*)dst = v;
                         }
                     }

@@ -8,11 +8,11 @@
 
 namespace fp8k {
 
-// Split-K workspace and split choice (gemm.hip).
+// Split choice (gemm.hip).  A split tile of the workspace holds the FP32
+// partial sums of one 32 x 64 tile (SPLIT_TILE_FLOATS floats).
 constexpr int64_t SPLIT_TILE_FLOATS = 32 * 64;
 int64_t split_slots();
-hipError_t get_workspace(hipStream_t s, float** ws, uint32_t** counters);
-int choose_splits(int64_t tiles, int64_t K, int per_cu);
+int choose_splits(int64_t tiles, int64_t K, int per_cu, int64_t capacity);
 
 inline int64_t tiles_of(int64_t M, int64_t N, int BM, int BN) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
@@ -22,16 +22,14 @@ hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
                       : launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_EXACT, false, FMT>(g, s);
 }
 
-// The same tile class with K split `splits` ways across workgroups
-// (tiles * splits <= the workspace's split tiles).
+// The same tile class with K split `splits` ways across workgroups, their
+// partials in the caller's workspace (tiles * splits <= its split tiles).
 template <int FMT, int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M>
 hipError_t launch_cfg_splitk(const GemmProblem& g, hipStream_t s, int32_t splits) {
     static_assert(BM * BN == SPLIT_TILE_FLOATS, "workspace sized for this tile");
-    if (tiles_of(g.M, g.N, BM, BN) * splits > split_slots()) return hipErrorInvalidValue;
-    float* ws = nullptr;
-    uint32_t* counters = nullptr;
-    const hipError_t e = get_workspace(s, &ws, &counters);
-    if (e != hipSuccess) return e;
+    if (tiles_of(g.M, g.N, BM, BN) * splits > g.ws_tiles || !g.ws || !g.counters) return hipErrorInvalidValue;
+    float* ws = g.ws;
+    uint32_t* counters = g.counters;
     return g.fast_acc
                ? launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_FAST, true, FMT>(g, s, splits, ws, counters)
                : launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_EXACT, true, FMT>(g, s, splits, ws, counters);
@@ -41,8 +39,9 @@ hipError_t launch_cfg_splitk(const GemmProblem& g, hipStream_t s, int32_t splits
 //  * M (rows per expert when grouped) <= 64: 32 x 64 tiles with each K step
 //    split over two wave groups -- many workgroups to stream B, HBM bound; a
 //    plain GEMM with fewer such tiles than half the GPU's workgroup slots
-//    also splits K across workgroups (measured on M = 16/32, N = 8192,
-//    K = 8192 with B out of HBM: 36.5 -> 26 us);
+//    also splits K across workgroups when the caller gave a workspace
+//    (measured on M = 16/32, N = 8192, K = 8192 with B out of HBM:
+//    36.5 -> 26 us);
 //  * M <= 1024: 128 x 128 tiles, 4 waves of 64 x 64 per K half, the K range
 //    split over two wave groups (more loads in flight per tile) -- unless a
 //    plain GEMM has so few of them that they would fill under half of the
@@ -58,7 +57,7 @@ hipError_t launch_gemm_t(const GemmProblem& g, hipStream_t s) {
     // split_slots() is twice the CU count
     const bool few_mid_tiles = plain && tiles_of(g.M, g.N, 128, 128) * 4 < split_slots();
     if (rows_per_problem <= 64 || (rows_per_problem <= 1024 && few_mid_tiles)) {
-        const int sp = plain ? choose_splits(tiles_of(g.M, g.N, 32, 64), g.K, 2) : 1;
+        const int sp = plain && g.ws_tiles > 0 ? choose_splits(tiles_of(g.M, g.N, 32, 64), g.K, 2, g.ws_tiles) : 1;
         if (sp > 1) return launch_cfg_splitk<FMT, 32, 64, 1, 2, 2, 4, 8>(g, s, sp);
         return launch_cfg<FMT, 32, 64, 1, 2, 2, 4, 8>(g, s);
     }

@@ -455,13 +455,13 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     // layout, coalesced; rows past M skipped) and counts itself in; the last
     // to arrive sums all the tile's partials in split order -- the same order
     // whichever split is last, so the result is deterministic -- and writes
-    // C.  Partials and counters are accessed only with device-scope atomics
-    // (coherent across the XCDs' L2s, no whole-cache write-back or
-    // invalidation): a split's stores have completed (vmcnt 0) before it
-    // counts itself in, and the last split reads only after its count came
-    // back.  No workgroup ever waits on another.  (With KS > 1 only wave
-    // group 0 holds the tile's sums; the other groups take part in the
-    // barriers and leave before the epilogue.)
+    // C.  Partials are stored and loaded as device-scope atomics (coherent
+    // across the XCDs' L2s); the arrival count is an acquire-release
+    // read-modify-write at device scope, so each split's partial stores
+    // happen before its count, and the count the last split reads happens
+    // before its loads of the partials.  No workgroup ever waits on another.
+    // (With KS > 1 only wave group 0 holds the tile's sums; the other groups
+    // take part in the barriers and leave before the epilogue.)
     if constexpr (SPLITK) {
         // the flag takes the first LDS word: past the first barrier below no
         // wave reads the stage or reduction buffers any more
@@ -514,15 +514,16 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     }
     if (ks > 0) return;
 
-    // Epilogue: the per-tensor (or per-expert) scale applied once to the sum
-    // (block scales are already folded in).  With KS > 1 the LDS scratch sits
-    // after the reduction buffer; otherwise every wave must first be done with
-    // the stage buffers.
+    // Epilogue: the per-tensor (or per-expert) scales applied once to the
+    // sum, one after the other (block scales are already folded in).  With
+    // KS > 1 the LDS scratch sits after the reduction buffer; otherwise every
+    // wave must first be done with the stage buffers.
     if constexpr (KS == 1) __syncthreads();
     using Store = TileStore<BF16, TM, TN>;
     lds_u8* scratch = lds + (KS > 1 ? C::RED : 0) + (wm * WN + wn) * Store::LDS_BYTES;
-    const float scale = (BLOCKED || E8) ? 1.0f : p.scale_a[t.expert] * p.scale_b[t.expert];
-    Store::run(p.C, acc, scale, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch,
+    const float sa = (BLOCKED || E8) ? 1.0f : p.scale_a[t.expert];
+    const float sb = (BLOCKED || E8) ? 1.0f : p.scale_b[t.expert];
+    Store::run(p.C, acc, sa, sb, t.m0 + wm * C::WTM, t.n0 + wn * C::WTN, t.M, N, t.c_row0, lane, scratch,
                p.out_f16 != 0);
 }
 

@@ -39,6 +39,12 @@ struct GemmProblem {
     const uint8_t* e8_a = nullptr;  // E8M0 tile exponents (block-scaled E8M0 GEMM only)
     const uint8_t* e8_b = nullptr;
     const uint32_t* sp_idx = nullptr;  // 2:4-sparse B (B then holds the compressed values)
+    // Split-K workspace (plain GEMM only; none: K is never split across
+    // workgroups): ws_tiles split tiles of FP32 partial sums at ws and one
+    // arrival counter per split tile at counters, zero between launches.
+    float* ws = nullptr;
+    uint32_t* counters = nullptr;
+    int64_t ws_tiles = 0;
 };
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
 

@@ -7,7 +7,12 @@
   bound above exceeds half a BF16 ulp of the exact value (heavy cancellation,
   where an FP32 accumulator cannot resolve the BF16 rounding), an element
   also passes if |C_gpu - C_exact| <= FP32 bound + 1 BF16 ulp; such elements
-  are counted and reported separately.
+  are counted separately, and their count must not exceed a ceiling,
+  8 + 2e-5 * (outputs compared) unless a test states otherwise.  An honest
+  FP32 accumulation needs the allowance on a few outputs per million of the
+  configurations' data (measured: 330 of 67M at 8192^3, 592 of 117M on the
+  4096 x 28672 x 8192 layer, 709 of 67M block-scaled); a kernel whose
+  accumulation lost precision would exceed the ceiling.
 * FP16 output: the same rule with binary16 ulps.
 """
 from __future__ import annotations
@@ -27,10 +32,12 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """The spacing of BF16 values at |x| (the subnormal step 2^-133 at and
+    near zero: frexp(0) reports exponent 0, which must not count)."""
     ax = np.abs(x)
     _, e = np.frexp(ax)                 # ax = f * 2^e, 0.5 <= f < 1
     ulp = np.ldexp(1.0, e - 8)          # 8 significand bits
-    return np.maximum(ulp, 2.0 ** -133)
+    return np.where(ax == 0, 2.0 ** -133, np.maximum(ulp, 2.0 ** -133))
 
 
 def check_f32(c_gpu: np.ndarray, exact: np.ndarray, sumabs_scaled: np.ndarray, what: str = ""):
@@ -45,9 +52,22 @@ def check_f32(c_gpu: np.ndarray, exact: np.ndarray, sumabs_scaled: np.ndarray, w
     return float(np.max(err / np.maximum(bound, 1e-300))) if c.size else 0.0
 
 
+ALLOW_FIXED, ALLOW_RATE = 8, 2e-5
+
+
+def _check_allowance(extra: int, max_extra, n: int, what: str):
+    if max_extra is None:
+        max_extra = ALLOW_FIXED + int(ALLOW_RATE * n)
+    if extra > max_extra:
+        raise AssertionError("%s: %d of %d outputs passed only under the cancellation allowance (ceiling %d)"
+                             % (what, extra, n, max_extra))
+
+
 def check_bf16(c_bits: np.ndarray, oracle_bits: np.ndarray, exact: np.ndarray, sumabs_scaled: np.ndarray,
-               what: str = ""):
-    """Returns (max ulp distance, count passed only under the cancellation allowance)."""
+               what: str = "", max_extra=None):
+    """Returns (max ulp distance, count passed only under the cancellation
+    allowance); that count must be at most max_extra (default: the ceiling
+    above)."""
     d = np.abs(bf16_ord(c_bits) - bf16_ord(oracle_bits))
     ok = d <= 1
     fbound = REL_F32 * sumabs_scaled
@@ -60,6 +80,7 @@ def check_bf16(c_bits: np.ndarray, oracle_bits: np.ndarray, exact: np.ndarray, s
         raise AssertionError("%s: %d of %d BF16 outputs more than 1 ulp from the oracle (worst %d ulp: got %#06x "
                              "want %#06x, exact %r)" % (what, int(bad.sum()), d.size, int(d.flat[i]),
                                                         int(c_bits.flat[i]), int(oracle_bits.flat[i]), exact.flat[i]))
+    _check_allowance(int(extra.sum()), max_extra, d.size, what)
     return int(d[ok].max()) if ok.any() else 0, int(extra.sum())
 
 
@@ -68,12 +89,15 @@ def f16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def f16_ulp(x: np.ndarray) -> np.ndarray:
-    _, e = np.frexp(np.abs(x))
-    return np.maximum(np.ldexp(1.0, e - 11), 2.0 ** -24)   # 11 significand bits, subnormal step 2^-24
+    """The spacing of binary16 values at |x| (11 significand bits; the
+    subnormal step 2^-24 at and near zero)."""
+    ax = np.abs(x)
+    _, e = np.frexp(ax)
+    return np.where(ax == 0, 2.0 ** -24, np.maximum(np.ldexp(1.0, e - 11), 2.0 ** -24))
 
 
 def check_f16(c_bits: np.ndarray, oracle_bits: np.ndarray, exact: np.ndarray, sumabs_scaled: np.ndarray,
-              what: str = ""):
+              what: str = "", max_extra=None):
     """The BF16 rule for IEEE binary16 output: within 1 ulp (monotone order of
     the bit patterns, +-Inf one step past the largest finite value) of the
     oracle's correctly rounded value, with the same cancellation allowance.
@@ -91,6 +115,7 @@ def check_f16(c_bits: np.ndarray, oracle_bits: np.ndarray, exact: np.ndarray, su
         raise AssertionError("%s: %d of %d FP16 outputs more than 1 ulp from the oracle (worst %d ulp: got %#06x "
                              "want %#06x, exact %r)" % (what, int(bad.sum()), d.size, int(d.flat[i]),
                                                         int(c_bits.flat[i]), int(oracle_bits.flat[i]), exact.flat[i]))
+    _check_allowance(int(extra.sum()), max_extra, d.size, what)
     return int(d[ok].max()) if ok.any() else 0, int(extra.sum())
 
 

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     for n in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
               "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_2of4", "fp8_gemm_sparse24",
               "fp8_quantize_grouped",
-              "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
+              "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_ws", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
               "fp8_status_string", "fp8_last_error"):
         assert n in names
 
@@ -79,6 +79,40 @@ def test_gemm_validation(kw, status):
     assert gemm(**kw) == status
     if status != P.FP8_OK:
         assert P.lib.fp8_last_error().decode() != ""
+
+
+def gemm_ws(ws=FAKE, nbytes=1 << 22, M=64, N=64, K=64, out=1, **kw):
+    return P.lib.fp8_gemm_ws(kw.get("A", FAKE), kw.get("B", FAKE), FAKE, FAKE, kw.get("C", FAKE), M, N, K, out,
+                             ws, nbytes, None)
+
+
+def test_gemm_ws_validation():
+    """fp8_gemm_ws checks its workspace before anything else reaches the GPU,
+    and otherwise validates exactly like fp8_gemm."""
+    assert gemm_ws(nbytes=-1) == P.FP8_ERR_INVALID_ARG
+    assert gemm_ws(ws=None, nbytes=8196) == P.FP8_ERR_INVALID_ARG       # null workspace with a size
+    assert gemm_ws(ws=FAKE_ODD) == P.FP8_ERR_INVALID_ARG                # misaligned workspace
+    assert gemm_ws(ws=None, nbytes=0, M=0) == P.FP8_OK                  # no workspace: plain fp8_gemm
+    assert gemm_ws(M=0) == P.FP8_OK
+    assert gemm_ws(N=40) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert gemm_ws(A=None) == P.FP8_ERR_INVALID_ARG
+    assert gemm_ws(out=1 | 0x800) == P.FP8_ERR_INVALID_ARG
+    assert "workspace" in (P.lib.fp8_gemm_ws(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 1, None, 16, None) and
+                           P.lib.fp8_last_error().decode())
+    # the header's sizes agree with the binding's
+    text = open(HEADER).read()
+    assert "#define FP8_GEMM_WS_TILE_BYTES %d" % P.FP8_GEMM_WS_TILE_BYTES in text
+    assert P.FP8_GEMM_WS_TILE_BYTES == 32 * 64 * 4 + 4
+
+
+def test_library_does_not_allocate():
+    """No entry point allocates device memory: the library's sources call no
+    allocator (scratch memory comes from the caller)."""
+    csrc = os.path.join(ROOT, "precision_dense_linear_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, f)).read()
+        for fn in ("hipMalloc", "hipFree", "hipExtMalloc", "hipMallocAsync", "hipHostMalloc"):
+            assert fn not in text, "%s calls %s" % (f, fn)
 
 
 def test_blockscaled_validation():

@@ -134,8 +134,9 @@ def test_formats_integer_exact_bit_for_bit(M, N, K, fa, fb, fast):
     both accumulation modes, all three output kinds."""
     qa, qb = int_codes((M, K), M + K, fa), int_codes((K, N), N + K, fb)
     A, B = gpu(qa), gpu(qb)
+    ws = P.gemm_workspace(DEV)   # (37, 1040, 4112) splits K across workgroups
     for kind in (F32, BF16, F16):
-        C = P.fp8_gemm(A, B, one(), one(), TORCH_OUT[kind], fast=fast, a_fmt=NAME[fa], b_fmt=NAME[fb])
+        C = P.fp8_gemm(A, B, one(), one(), TORCH_OUT[kind], fast=fast, a_fmt=NAME[fa], b_fmt=NAME[fb], workspace=ws)
         bits, _, _ = oracle.gemm_rows_fmt(qa, qb, fa, fb, 1.0, 1.0, kind)
         got = to_bits(C)
         assert np.array_equal(got, bits), "kind %d: %d mismatches" % (kind, int((got != bits).sum()))

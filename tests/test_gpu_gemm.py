@@ -41,10 +41,10 @@ def compare(C, bits, exact, sab_scaled, kind, rows, what):
     return check_bf16(got, bits, exact, sab_scaled, what)
 
 
-def pertensor_end_to_end(a, b, kind, rows=None, what=""):
+def pertensor_end_to_end(a, b, kind, rows=None, what="", workspace=None):
     qa, sa, _ = P.fp8_quantize(gpu(a))
     qb, sb, _ = P.fp8_quantize(gpu(b))
-    C = P.fp8_gemm(qa, qb, sa, sb, torch.float32 if kind == F32 else torch.bfloat16)
+    C = P.fp8_gemm(qa, qb, sa, sb, torch.float32 if kind == F32 else torch.bfloat16, workspace=workspace)
     torch.cuda.synchronize()
     oa, osa, _ = oracle.quantize_pertensor(a)
     ob, osb, _ = oracle.quantize_pertensor(b)
@@ -133,9 +133,10 @@ def test_random_ragged_f32(M, N, K):
 
 
 # ------------------------------------------------------------------ split-K
-# M <= 64 with few 32 x 64 tiles splits K over workgroups.  With 256 CUs the
-# shapes below take 2, 8, 4 and 8 splits; the K stage counts (4, 17, 9, 32)
-# give even and uneven K ranges, the last one ending in a partial stage.
+# fp8_gemm_ws: M <= 64 with few 32 x 64 tiles splits K over workgroups.  With
+# 256 CUs the shapes below take 2, 8, 4 and 8 splits; the K stage counts (4,
+# 17, 9, 32) give even and uneven K ranges, the last one ending in a partial
+# stage.
 SPLITK_SHAPES = [(1, 512, 1024), (37, 1040, 4112), (64, 2048, 2304), (20, 96, 8192)]
 
 
@@ -145,20 +146,37 @@ SPLITK_SHAPES = [(1, 512, 1024), (37, 1040, 4112), (64, 2048, 2304), (20, 96, 81
 def test_splitk_integer_exact_bit_for_bit(M, N, K, fast, kind):
     """Integer operands make the sum exact in any order, so every split's
     partial, the fixed-order sum and the ragged row/column edges must give
-    the oracle's value bit for bit."""
+    the oracle's value bit for bit -- with the workspace (split) and without
+    it (one workgroup per tile)."""
     qa, va = int_codes((M, K), M * 5 + K, lim=8)
     qb, vb = int_codes((K, N), N * 3 + K, lim=8)
-    C = P.fp8_gemm(gpu(qa), gpu(qb), scalar(1.0), scalar(1.0), torch.float32 if kind == F32 else torch.bfloat16,
-                   fast=fast)
     bits, exact, _ = oracle.gemm_rows(qa, qb, 1.0, 1.0, kind)
-    got = to_bits(C)
-    assert np.array_equal(got, bits), "%d mismatches" % int((got != bits).sum())
+    for ws in (P.gemm_workspace(DEV), None):
+        C = P.fp8_gemm(gpu(qa), gpu(qb), scalar(1.0), scalar(1.0), torch.float32 if kind == F32 else torch.bfloat16,
+                       fast=fast, workspace=ws)
+        got = to_bits(C)
+        assert np.array_equal(got, bits), "%d mismatches (workspace: %s)" % (int((got != bits).sum()), ws is not None)
 
 
 @pytest.mark.parametrize("M,N,K", [(48, 3072, 8192), (37, 1040, 4112)])
 def test_splitk_random_f32(M, N, K):
     a, b = W.pertensor_pair(M, N, K, seed=M * N + K)
-    pertensor_end_to_end(a, b, F32, what="split-K %dx%dx%d" % (M, N, K))
+    pertensor_end_to_end(a, b, F32, what="split-K %dx%dx%d" % (M, N, K), workspace=P.gemm_workspace(DEV))
+
+
+def test_splitk_small_workspace_limits_the_splits():
+    """A workspace of only a few split tiles bounds tiles x splits: 16 tiles
+    with room for 40 split tiles run 2 splits each (a third would not fit),
+    and room for 31 leaves the call unsplit; both exact on integer codes."""
+    M, N, K = 20, 1024, 8192
+    qa, _ = int_codes((M, K), 11, lim=8)
+    qb, _ = int_codes((K, N), 12, lim=8)
+    bits, _, _ = oracle.gemm_rows(qa, qb, 1.0, 1.0, F32)
+    for tiles in (40, 31):
+        ws = P.gemm_workspace(DEV, tiles * P.FP8_GEMM_WS_TILE_BYTES)
+        C = P.fp8_gemm(gpu(qa), gpu(qb), scalar(1.0), scalar(1.0), torch.float32, workspace=ws)
+        assert np.array_equal(to_bits(C), bits)
+        assert torch.count_nonzero(ws[tiles * 8192:]).item() == 0    # counters back at zero
 
 
 def test_splitk_repeated_calls_other_shapes_and_two_streams():
@@ -171,29 +189,30 @@ def test_splitk_repeated_calls_other_shapes_and_two_streams():
         qb, sb, _ = P.fp8_quantize(gpu(b))
         return qa, qb, sa, sb
 
+    ws1, ws2 = P.gemm_workspace(DEV), P.gemm_workspace(DEV)
     x = operands(40, 4096, 4096, 3)   # 128 tiles, 4 splits
     y = operands(16, 1024, 8192, 4)   # 16 tiles, 8 splits
-    Cx = P.fp8_gemm(*x, torch.float32)
-    Cy = P.fp8_gemm(*y, torch.bfloat16)
+    Cx = P.fp8_gemm(*x, torch.float32, workspace=ws1)
+    Cy = P.fp8_gemm(*y, torch.bfloat16, workspace=ws1)
     torch.cuda.synchronize()
     for _ in range(3):
-        assert torch.equal(P.fp8_gemm(*x, torch.float32), Cx)
-        assert torch.equal(P.fp8_gemm(*y, torch.bfloat16).view(torch.int16), Cy.view(torch.int16))
+        assert torch.equal(P.fp8_gemm(*x, torch.float32, workspace=ws1), Cx)
+        assert torch.equal(P.fp8_gemm(*y, torch.bfloat16, workspace=ws1).view(torch.int16), Cy.view(torch.int16))
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
     outs = []
     for _ in range(4):
         with torch.cuda.stream(s1):
-            o1 = P.fp8_gemm(*x, torch.float32)
+            o1 = P.fp8_gemm(*x, torch.float32, workspace=ws1)
         with torch.cuda.stream(s2):
-            o2 = P.fp8_gemm(*y, torch.bfloat16)
+            o2 = P.fp8_gemm(*y, torch.bfloat16, workspace=ws2)
         outs.append((o1, o2))
     torch.cuda.synchronize()
     for o1, o2 in outs:
         assert torch.equal(o1, Cx)
         assert torch.equal(o2.view(torch.int16), Cy.view(torch.int16))
     a, b = W.pertensor_pair(40, 4096, 4096, seed=3)
-    pertensor_end_to_end(a, b, F32, what="split-K 40x4096x4096 (oracle)")
+    pertensor_end_to_end(a, b, F32, what="split-K 40x4096x4096 (oracle)", workspace=ws1)
 
 
 # ------------------------------------------------------------------ block-scaled

@@ -30,10 +30,11 @@ def test_max_k(fast):
     M, N, K = 33, 32, 1 << 23
     qa, qb = unit_codes((M, K), 1), unit_codes((K, N), 2)
     one = torch.ones(1, device=DEV)
-    C = P.fp8_gemm(gpu(qa), gpu(qb), one, one, torch.float32, fast=fast)
     bits, exact, _ = oracle.gemm_rows(qa, qb, 1.0, 1.0, oracle.F32)
     assert np.abs(exact).max() < 2 ** 24
-    assert np.array_equal(to_bits(C), bits)
+    for ws in (P.gemm_workspace(DEV), None):     # split over 8 workgroups, and unsplit
+        C = P.fp8_gemm(gpu(qa), gpu(qb), one, one, torch.float32, fast=fast, workspace=ws)
+        assert np.array_equal(to_bits(C), bits)
 
 
 def test_k_beyond_max_rejected():

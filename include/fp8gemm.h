@@ -247,6 +247,26 @@ fp8_status fp8_gemm_ws(const uint8_t* A, const uint8_t* B, const float* scale_a,
                        void* stream);
 
 /*
+ * fp8_gemm_ws for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation):
+ * the split-K workspace is the library's own static device array of
+ * FP8_GEMM_WORKSPACE_BYTES (512 split tiles), one per GPU the library runs
+ * on, held until the process ends.  Same operation, arguments (less the
+ * workspace), checks and errors as fp8_gemm_ws with a workspace of that
+ * size, and bit-identical results.  The split count is chosen to fit the
+ * array (tiles x splits <= 512), so no problem size needs more scratch than
+ * it holds.  No allocation: the first call on a device looks up the array's
+ * address there and clears its arrival counters with a kernel on `stream`
+ * (FP8_ERR_HIP if that fails); every completed call leaves them at zero.
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (on several streams, from several host threads, or graphs
+ * replayed concurrently) race and give wrong results -- issue them in order
+ * on one stream.
+ */
+fp8_status fp8_gemm_noalloc(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
+                            int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream);
+
+/*
  * Block-scaled FP8 GEMM with 32x32 tile scales ([P3] parameter paragraph:
  * 32x32 scale blocks; the warp-specialisation paragraph's promotion of
  * partial products on the general-purpose cores):

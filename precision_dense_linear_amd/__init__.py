@@ -15,6 +15,7 @@ Entry points (same names as the C ABI):
     fp8_quantize_grouped(x, offsets)         -> (q, scales, amax)
     fp8_quantize_grouped_e5m2(x, offsets)    -> (q, scales, amax)
     fp8_gemm(A, B, scale_a, scale_b, out_dtype)   (fp8_gemm_ws with workspace=)
+    fp8_gemm_noalloc(A, B, scale_a, scale_b, out_dtype)
     gemm_workspace(device)                   -> zeroed split-K workspace (torch.uint8)
     fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype, block=32 | 64)
     fp8_gemm_blockscaled_e8m0(A, B, e_a, e_b, out_dtype)
@@ -46,8 +47,8 @@ FP8_GEMM_WORKSPACE_BYTES = 512 * FP8_GEMM_WS_TILE_BYTES
 SYMBOLS = ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
            "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_2of4",
            "fp8_gemm_sparse24", "fp8_quantize_grouped",
-           "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_ws", "fp8_gemm_blockscaled", "fp8_grouped_gemm",
-           "fp8_status_string", "fp8_last_error")
+           "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_ws", "fp8_gemm_noalloc", "fp8_gemm_blockscaled",
+           "fp8_grouped_gemm", "fp8_status_string", "fp8_last_error")
 
 
 class FP8Error(RuntimeError):
@@ -75,12 +76,14 @@ def _load():
     L.fp8_quantize_grouped_e5m2.argtypes = [P, i64, i64, P, i32, P, P, P, P]
     L.fp8_gemm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_gemm_ws.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P, i64, P]
+    L.fp8_gemm_noalloc.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_gemm_blockscaled.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i64, i64, i64, i32, P]
     for f in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
               "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_2of4",
            "fp8_gemm_sparse24", "fp8_quantize_grouped",
-              "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_ws", "fp8_gemm_blockscaled", "fp8_grouped_gemm"):
+              "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_ws", "fp8_gemm_noalloc", "fp8_gemm_blockscaled",
+              "fp8_grouped_gemm"):
         getattr(L, f).restype = st
     L.fp8_status_string.restype = ctypes.c_char_p
     L.fp8_status_string.argtypes = [i32]
@@ -275,6 +278,25 @@ def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=No
                                                   K, code | flags, _ptr(workspace),
                                                   workspace.numel() * workspace.element_size(),
                                                   _stream(A.device, stream)))
+    return C
+
+
+def fp8_gemm_noalloc(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=None, fast=False, a_fmt=None,
+                     b_fmt=None):
+    """fp8_gemm with K split across workgroups where that fills the GPU, the
+    partial sums in the library's own static device array (no allocation by
+    the library; C is allocated here only when not given).  Calls on one GPU
+    must not overlap in time."""
+    flags = _fmt_flag(A, a_fmt, FP8_A_E5M2) | _fmt_flag(B, b_fmt, FP8_B_E5M2) | (FP8_ACC_FAST if fast else 0)
+    A, B = _codes(A), _codes(B)
+    M, K = A.shape
+    N = B.shape[1]
+    _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
+    code = _out_code(out_dtype)
+    C = _out_tensor(C, (M, N), code, A.device)
+    with torch.cuda.device(A.device):
+        _check("fp8_gemm_noalloc", lib.fp8_gemm_noalloc(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N,
+                                                        K, code | flags, _stream(A.device, stream)))
     return C
 
 

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fp8gemm.h"
 #include "launch.h"
 
@@ -107,6 +109,82 @@ fp8_status quantize_grouped(const float* x, int64_t rows, int64_t cols, const in
         what);
 }
 
+// Argument checks of the per-tensor GEMM (fp8_gemm and its variants).
+fp8_status check_pertensor(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b,
+                           const void* C, int64_t M, int64_t N, int64_t K, int32_t out_dtype) {
+    fp8_status st = check_gemm_common(A, B, C, M, N, K, out_dtype, FP8_ACC_FAST | FP8_A_E5M2 | FP8_B_E5M2);
+    if (st != FP8_OK) return st;
+    if (!scale_a || !scale_b) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
+    if (K % 16 || N % 16)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld and N=%lld must be multiples of 16", (long long)K, (long long)N);
+    return FP8_OK;
+}
+
+// The per-tensor GEMM with an optional split-K workspace (ws_tiles split
+// tiles: FP32 partial sums first, then one arrival counter per split tile).
+// Arguments already checked.
+fp8_status launch_pertensor(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
+                            int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* ws, int64_t ws_tiles,
+                            void* stream, const char* what) {
+    if (M == 0 || N == 0) return ok();
+    fp8k::GemmProblem g{A, B, C, scale_a, scale_b, nullptr, 0, M, N, K, 0, 0, 0, 0};
+    decode_out(out_dtype, g);
+    if (ws && ws_tiles > 0) {
+        g.ws = static_cast<float*>(ws);
+        g.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + ws_tiles * kSplitTileFloatBytes);
+        g.ws_tiles = ws_tiles;
+    }
+    return from_hip(fp8k::launch_gemm(g, (hipStream_t)stream), what);
+}
+
+fp8_status gemm_pertensor(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
+                          int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* ws, int64_t ws_tiles,
+                          void* stream, const char* what) {
+    const fp8_status st = check_pertensor(A, B, scale_a, scale_b, C, M, N, K, out_dtype);
+    if (st != FP8_OK) return st;
+    return launch_pertensor(A, B, scale_a, scale_b, C, M, N, K, out_dtype, ws, ws_tiles, stream, what);
+}
+
+// fp8_gemm_noalloc's split-K workspace: one array per GPU, in the library's
+// own device memory, for callers that cannot allocate.  Host code never uses
+// the array's name as an address: at the first call on a device its address
+// there is looked up with hipGetSymbolAddress (with that device current) and
+// kept in scratch_ptr[device].
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[FP8_GEMM_WORKSPACE_BYTES];
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_words(uint32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// The device address of the current device's scratch array (set up on the
+// first call there: the symbol lookup, then a fill kernel on `s` that clears
+// the arrival counters, which every completed call leaves at zero again).
+fp8_status scratch_for_current_device(hipStream_t s, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FP8_ERR_HIP, "fp8_gemm_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(FP8_ERR_INVALID_ARG, "fp8_gemm_noalloc: device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(FP8_ERR_HIP, "fp8_gemm_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+        constexpr int tiles = FP8_GEMM_WORKSPACE_BYTES / FP8_GEMM_WS_TILE_BYTES;
+        uint32_t* counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ptr) + tiles * kSplitTileFloatBytes);
+        hipLaunchKernelGGL(zero_words, dim3((tiles + 255) / 256), dim3(256), 0, s, counters, tiles);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(FP8_ERR_HIP, "fp8_gemm_noalloc: clearing the counters: %s", hipGetErrorString(e));
+        scratch_ptr[dev] = ptr;
+    }
+    *out = scratch_ptr[dev];
+    return FP8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -166,27 +244,6 @@ fp8_status fp8_quantize_grouped_e5m2(const float* x, int64_t rows, int64_t cols,
     return quantize_grouped(x, rows, cols, offsets, groups, q, scales, amax, 1, stream, "fp8_quantize_grouped_e5m2");
 }
 
-// The per-tensor GEMM with an optional split-K workspace (ws_tiles split
-// tiles: FP32 partial sums first, then one arrival counter per split tile).
-fp8_status gemm_pertensor(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
-                          int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* ws, int64_t ws_tiles,
-                          void* stream, const char* what) {
-    fp8_status st = check_gemm_common(A, B, C, M, N, K, out_dtype, FP8_ACC_FAST | FP8_A_E5M2 | FP8_B_E5M2);
-    if (st != FP8_OK) return st;
-    if (!scale_a || !scale_b) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
-    if (K % 16 || N % 16)
-        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "K=%lld and N=%lld must be multiples of 16", (long long)K, (long long)N);
-    if (M == 0 || N == 0) return ok();
-    fp8k::GemmProblem g{A, B, C, scale_a, scale_b, nullptr, 0, M, N, K, 0, 0, 0, 0};
-    decode_out(out_dtype, g);
-    if (ws && ws_tiles > 0) {
-        g.ws = static_cast<float*>(ws);
-        g.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + ws_tiles * kSplitTileFloatBytes);
-        g.ws_tiles = ws_tiles;
-    }
-    return from_hip(fp8k::launch_gemm(g, (hipStream_t)stream), what);
-}
-
 fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
                     int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
     return gemm_pertensor(A, B, scale_a, scale_b, C, M, N, K, out_dtype, nullptr, 0, stream, "fp8_gemm");
@@ -200,6 +257,20 @@ fp8_status fp8_gemm_ws(const uint8_t* A, const uint8_t* B, const float* scale_a,
     if (!aligned16(workspace)) return fail(FP8_ERR_INVALID_ARG, "the workspace must be 16-byte aligned");
     return gemm_pertensor(A, B, scale_a, scale_b, C, M, N, K, out_dtype, workspace,
                           workspace_bytes / FP8_GEMM_WS_TILE_BYTES, stream, "fp8_gemm_ws");
+}
+
+fp8_status fp8_gemm_noalloc(const uint8_t* A, const uint8_t* B, const float* scale_a, const float* scale_b, void* C,
+                            int64_t M, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
+    // argument checks first (no device work for a rejected or empty call),
+    // then the scratch array of the current device
+    fp8_status st = check_pertensor(A, B, scale_a, scale_b, C, M, N, K, out_dtype);
+    if (st != FP8_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    void* ws = nullptr;
+    st = scratch_for_current_device((hipStream_t)stream, &ws);
+    if (st != FP8_OK) return st;
+    return launch_pertensor(A, B, scale_a, scale_b, C, M, N, K, out_dtype, ws,
+                            FP8_GEMM_WORKSPACE_BYTES / FP8_GEMM_WS_TILE_BYTES, stream, "fp8_gemm_noalloc");
 }
 
 fp8_status fp8_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,

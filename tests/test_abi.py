@@ -105,6 +105,19 @@ def test_gemm_ws_validation():
     assert P.FP8_GEMM_WS_TILE_BYTES == 32 * 64 * 4 + 4
 
 
+def test_gemm_noalloc_validation():
+    """fp8_gemm_noalloc rejects bad arguments, and returns at once for an
+    empty problem, before it touches any device (its scratch set-up included)."""
+    f = P.lib.fp8_gemm_noalloc
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 40, 64, 1, None) == P.FP8_ERR_UNSUPPORTED_SHAPE
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 64, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 1 | 0x800, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 64, 64, 1, None) == P.FP8_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 1 | P.FP8_ACC_FAST, None) == P.FP8_OK
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 0, 64, 1, None) == P.FP8_OK
+
+
 def test_library_does_not_allocate():
     """No entry point allocates device memory: the library's sources call no
     allocator (scratch memory comes from the caller)."""

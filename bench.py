@@ -123,7 +123,7 @@ def parse():
     ap.add_argument("--workload", default="gemm8192",
                     choices=["gemm8192", "gemm1024", "gemm256", "llm16", "llm128", "llm4096", "blockscaled8192",
                              "moe", "mixed8192", "blockscaled8192_64", "blockscaled8192_e8m0", "sparse8192",
-                             "sparse_llm4096"])
+                             "sparse_llm4096", "attn4096", "attn4096_causal"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-vendor", action="store_true", help="skip timing the vendor GEMM library for comparison")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -186,6 +186,16 @@ class Workload:
             a, b = W.blockscaled_pair(8192, 8192, 8192)
             self.desc = ("block-scaled FP8 GEMM M=N=K=8192 with power-of-two (E8M0) 32x32 tile scales applied by the "
                          "FP8 matrix cores, BF16 out; tile factors 10^U(-2,2)")
+        elif name.startswith("attn"):
+            self.kind = "attn"
+            self.causal = name.endswith("causal")
+            self.heads, S, D = 32, 4096, 128
+            q, k, v = W.attention_qkv(self.heads, S, S, D)
+            a, b = q, np.stack([k, v])
+            self.M, self.N, self.K = S, D, S          # seq_q, head_dim, seq_kv
+            self.desc = ("FP8 multi-head attention: 32 heads, seq_q = seq_kv = 4096, head_dim 128, %s, BF16 out; "
+                         "Q, K, V FP32 N(0,1) quantized per tensor to e4m3fn on device"
+                         % ("causal" if self.causal else "non-causal"))
         elif name.startswith("blockscaled8192"):
             self.kind = "block"
             self.block = 64 if name.endswith("_64") else 32
@@ -212,7 +222,10 @@ class Workload:
             self.qi = torch.empty((self.K // 32, self.N), dtype=torch.int32, device=dev)
         self.C = torch.empty((self.M, self.N), dtype=self.out, device=dev)
         self.ws = P.gemm_workspace(dev)  # split-K workspace (used by the few-tile shapes, M <= 64)
-        if self.kind in ("pertensor", "sparse"):
+        if self.kind == "attn":
+            self.C = torch.empty(a.shape, dtype=self.out, device=dev)
+            self.sa, self.aa, self.sb, self.ab, self.sv, self.av = (torch.empty(1, device=dev) for _ in range(6))
+        elif self.kind in ("pertensor", "sparse"):
             self.sa, self.aa = (torch.empty(1, device=dev) for _ in range(2))
             self.sb, self.ab = (torch.empty(1, device=dev) for _ in range(2))
         elif self.kind == "block_e8":
@@ -226,10 +239,17 @@ class Workload:
             self.sa, self.aa = (torch.empty(self.E, device=dev) for _ in range(2))
             self.sb, self.ab = (torch.empty(self.E, device=dev) for _ in range(2))
         self.flops = 2.0 * self.M * self.N * self.K
+        if self.kind == "attn":    # both products over the visible (query, key) pairs
+            pairs = self.M * (self.M + 1) / 2 if self.causal else float(self.M) * self.K
+            self.flops = 4.0 * self.heads * pairs * self.N
 
     def quantize(self):
         P = self.P
-        if self.kind == "pertensor":
+        if self.kind == "attn":
+            P.fp8_quantize(self.A, self.qa, self.sa, self.aa)
+            P.fp8_quantize(self.B[0], self.qb[0], self.sb, self.ab)
+            P.fp8_quantize(self.B[1], self.qb[1], self.sv, self.av)
+        elif self.kind == "pertensor":
             P.fp8_quantize(self.A, self.qa, self.sa, self.aa)
             (P.fp8_quantize_e5m2 if self.b_e5m2 else P.fp8_quantize)(self.B, self.qb, self.sb, self.ab)
         elif self.kind == "sparse":
@@ -250,7 +270,9 @@ class Workload:
         P = self.P
         qa = self.qa if qa is None else qa
         qb = self.qb if qb is None else qb
-        if self.kind == "pertensor":
+        if self.kind == "attn":
+            P.fp8_attention(qa, qb[0], qb[1], self.sa, self.sb, self.sv, None, self.causal, self.out, O=self.C)
+        elif self.kind == "pertensor":
             P.fp8_gemm(qa, qb, self.sa, self.sb, self.out, C=self.C, fast=fast,
                        b_fmt="e5m2" if self.b_e5m2 else "e4m3", workspace=self.ws)
         elif self.kind == "sparse":
@@ -270,6 +292,8 @@ class Workload:
     def gemm_bytes(self):
         """Algorithmic HBM bytes of one GEMM launch: A and B codes once, C once."""
         osz = 4 if self.out == self.torch.float32 else 2
+        if self.kind == "attn":    # Q, K, V codes once, O once
+            return self.qa.numel() + self.qb.numel() + self.C.numel() * osz
         if self.kind == "moe":
             return self.M * self.K + self.E * self.K * self.N + self.M * self.N * osz
         t = getattr(self, "block", 32)
@@ -307,6 +331,21 @@ def cpu_baseline(w: Workload, rows: int):
         t0 = time.perf_counter()
         oracle.gemm_rows(qa, qb, sa, sb, oracle.BF16 if w.out != w.torch.float32 else oracle.F32, rows=sel)
         tg = time.perf_counter() - t0
+    elif w.kind == "attn":
+        from oracle import attention as OA
+        hs = 4   # heads in the sample (of 32)
+        qq, sq, _ = oracle.quantize_pertensor(w.a_host)
+        qk, sk, _ = oracle.quantize_pertensor(w.b_host[0])
+        qv, sv, _ = oracle.quantize_pertensor(w.b_host[1])
+        tq = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        OA.attention(qq[:hs], qk[:hs], qv[:hs], sq, sk, sv, 1.0 / np.sqrt(w.N), w.causal)
+        tg = time.perf_counter() - t0
+        t_step = tq + tg * w.heads / hs
+        return {"value": round(w.flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": "quantize Q, K, V (%.2fs), float64 attention of %d of %d heads (%.2fs); scaled to one "
+                          "full step = %.1fs" % (tq, hs, w.heads, tg, t_step)}
     else:
         return None
     t_step = tqa * M / r + tqb + tg * M / r
@@ -325,6 +364,8 @@ def vendor_reference(w: Workload):
     takes) and its BF16 GEMM on the codes widened to BF16, with B as an N x K
     weight (its fastest layout) and as the row-major K x N matrix."""
     torch = w.torch
+    if w.kind == "attn":
+        return vendor_attention(w)
     if w.kind != "pertensor" or w.b_e5m2 or w.out != torch.bfloat16:
         return None
     out = {"library": "hipBLASLt via torch._scaled_mm (FP8), torch.nn.functional.linear and torch.matmul (BF16)"}
@@ -358,6 +399,33 @@ def vendor_reference(w: Workload):
     out["bf16_b_row_major"] = timed(lambda: torch.matmul(a16, b16))
     del a16, b16, bt8
     return out
+
+
+def vendor_attention(w: Workload):
+    """Context, not part of the step: torch's scaled_dot_product_attention in
+    BF16 (the ROCm fused attention kernels) on the same values, the codes
+    widened to BF16 with the scales folded into Q and V, timed like the
+    kernel above."""
+    torch = w.torch
+    q16 = (w.qa.view(torch.float8_e4m3fn).to(torch.float32) * (w.sa * w.sb)).to(torch.bfloat16)[None]
+    k16 = w.qb[0].view(torch.float8_e4m3fn).to(torch.bfloat16)[None]
+    v16 = (w.qb[1].view(torch.float8_e4m3fn).to(torch.float32) * w.sv).to(torch.bfloat16)[None]
+    f = lambda: torch.nn.functional.scaled_dot_product_attention(q16, k16, v16, is_causal=w.causal,
+                                                                  scale=1.0 / np.sqrt(w.N))
+    try:
+        for _ in range(3):
+            f()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for s_, e_ in ev:
+            s_.record()
+            f()
+            e_.record()
+        torch.cuda.synchronize()
+        us = float(np.median([s_.elapsed_time(e_) for s_, e_ in ev])) * 1e3
+        return {"library": "torch.nn.functional.scaled_dot_product_attention (BF16)",
+                "bf16": {"median_us": round(us, 2), "tflops": round(w.flops / (us * 1e-6) / 1e12, 2)}}
+    except Exception as e:  # no fused attention on this build
+        return {"library": "torch.nn.functional.scaled_dot_product_attention (BF16)", "error": repr(e)[:200]}
 
 
 def main():
@@ -406,7 +474,7 @@ def main():
 
     # the native-FP8-accumulation GEMM (FP8_ACC_FAST), timed the same way, outside the timed region
     fast = None
-    if w.kind not in ("block", "block_e8", "sparse"):
+    if w.kind not in ("block", "block_e8", "sparse", "attn"):
         for _ in range(3):
             w.gemm(fast=True)
         fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -519,7 +587,8 @@ def main():
                   else "gemm_kernel MODE_BLOCK (fp8_gemm_blockscaled)"),
         "block_e8": "gemm_kernel MODE_E8M0 (fp8_gemm_blockscaled_e8m0)",
         "sparse": "gemm_kernel MODE_SPARSE (fp8_gemm_sparse24)",
-        "moe": "gemm_kernel (fp8_grouped_gemm)"}[w.kind]
+        "moe": "gemm_kernel (fp8_grouped_gemm)",
+        "attn": "attention_kernel (fp8_attention)"}[w.kind]
     roof["avg_kernel_us"] = round((avg_gemm_ms if mfma_bound else hbm_ms) * 1e3, 2)
     vendor = None if args.no_vendor else vendor_reference(w)
     mhz = sclk.mean_mhz()

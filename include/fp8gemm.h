@@ -359,6 +359,39 @@ fp8_status fp8_grouped_gemm(const uint8_t* A, const uint8_t* B, const int32_t* o
                             const float* scale_a, const float* scale_b, void* C,
                             int64_t T, int64_t N, int64_t K, int32_t out_dtype, void* stream);
 
+/*
+ * FP8 multi-head attention ("Leveraging CUTLASS kernel naming in Triton for
+ * a 100 TFLOPS FP8 tensor-core speed-up in multi-head attention",
+ * blog.hotdry.top: the fp8_mha_kernel sketch -- an FP8 Q K^T with the
+ * softmax and the accumulation of V fused behind it -- read as standard
+ * scaled dot-product attention).  For every head h and query i:
+ *     S[i, j] = (scale_q * scale_k * softmax_scale) * sum_d Q[h, i, d] * K[h, j, d]
+ *     O[h, i, d] = scale_v * sum_j softmax_j(S[i, :]) * V[h, j, d]
+ * over the keys visible to i: all of them, or with causal = 1 those with
+ * j <= i + seq_kv - seq_q; a query that sees no key gets O = 0.
+ * Q: batch_heads x seq_q x head_dim E4M3 codes, K and V: batch_heads x
+ * seq_kv x head_dim, O: batch_heads x seq_q x head_dim of out_dtype
+ * (FP8_OUT_F32, _BF16 or _F16, no flags); all row-major, head_dim
+ * contiguous, 16-byte aligned.  scale_q, scale_k, scale_v: one float each on
+ * the device (as fp8_quantize writes them); softmax_scale on the host,
+ * positive and finite (1/sqrt(head_dim) for standard attention).
+ * Arithmetic: the codes are widened exactly to BF16, both products are
+ * exact and accumulate in FP32, the softmax is an online FP32 one over
+ * 64-key blocks; each probability enters the second product rounded to
+ * BF16, and the row sum adds the same rounded values.  Error bound per
+ * output (w the exact softmax weights of the row): |O - O_exact| <=
+ *     (1.01 * (2^-8 + 4 dS) + 2^-23 * (2 seq_kv + 16)) * scale_v * sum_j w_j |V[j, d]|
+ *     + 2^-22 |O_exact| + 1 ulp of the output type at |O_exact| + that bound,
+ * dS = 2^-24 * (head_dim * max_j A[i, j] + 6 max_j |S[i, j]|), A the score
+ * with every product taken in magnitude (max over the visible keys).
+ * batch_heads, seq_q, seq_kv >= 0; head_dim 64 or 128 (else
+ * FP8_ERR_UNSUPPORTED_SHAPE); seq_q, seq_kv < 2^31 / head_dim.
+ */
+fp8_status fp8_attention(const uint8_t* Q, const uint8_t* K, const uint8_t* V, const float* scale_q,
+                         const float* scale_k, const float* scale_v, void* O, int64_t batch_heads, int64_t seq_q,
+                         int64_t seq_kv, int64_t head_dim, float softmax_scale, int32_t causal, int32_t out_dtype,
+                         void* stream);
+
 /* Static name of a status code ("FP8_OK", ...); never NULL. */
 const char* fp8_status_string(int32_t status);
 

@@ -22,6 +22,7 @@ Entry points (same names as the C ABI):
     fp8_quantize_2of4(w)                     -> (vals, idx, scale, amax)
     fp8_gemm_sparse24(A, vals, idx, scale_a, scale_b, out_dtype)
     fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype)
+    fp8_attention(Q, K, V, scale_q, scale_k, scale_v, softmax_scale, causal, out_dtype)
 FP8 codes are passed as torch.uint8 (E4M3 unless a_fmt / b_fmt say "e5m2"),
 torch.float8_e4m3fn or torch.float8_e5m2 tensors; out_dtype is
 torch.float32, torch.bfloat16 or torch.float16.
@@ -48,7 +49,7 @@ SYMBOLS = ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_qua
            "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_2of4",
            "fp8_gemm_sparse24", "fp8_quantize_grouped",
            "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_ws", "fp8_gemm_noalloc", "fp8_gemm_blockscaled",
-           "fp8_grouped_gemm", "fp8_status_string", "fp8_last_error")
+           "fp8_grouped_gemm", "fp8_attention", "fp8_status_string", "fp8_last_error")
 
 
 class FP8Error(RuntimeError):
@@ -79,11 +80,12 @@ def _load():
     L.fp8_gemm_noalloc.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_gemm_blockscaled.argtypes = [P, P, P, P, P, i64, i64, i64, i32, P]
     L.fp8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i64, i64, i64, i32, P]
+    L.fp8_attention.argtypes = [P, P, P, P, P, P, P, i64, i64, i64, i64, ctypes.c_float, i32, i32, P]
     for f in ("fp8_quantize", "fp8_quantize_e5m2", "fp8_quantize_blocked", "fp8_quantize_blocked64",
               "fp8_quantize_blocked_e8m0", "fp8_gemm_blockscaled_e8m0", "fp8_quantize_2of4",
            "fp8_gemm_sparse24", "fp8_quantize_grouped",
               "fp8_quantize_grouped_e5m2", "fp8_gemm", "fp8_gemm_ws", "fp8_gemm_noalloc", "fp8_gemm_blockscaled",
-              "fp8_grouped_gemm"):
+              "fp8_grouped_gemm", "fp8_attention"):
         getattr(L, f).restype = st
     L.fp8_status_string.restype = ctypes.c_char_p
     L.fp8_status_string.argtypes = [i32]
@@ -387,3 +389,24 @@ def fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype=torch.bfloat16, 
                                                         _ptr(scale_b), _ptr(C), T, N, K, code | flags,
                                                         _stream(A.device, stream)))
     return C
+
+
+def fp8_attention(Q, K, V, scale_q, scale_k, scale_v, softmax_scale=None, causal=False, out_dtype=torch.bfloat16,
+                  O=None, stream=None):
+    """Multi-head attention on E4M3 codes: Q [BH, Sq, D], K and V [BH, Skv, D] (D = 64 or 128),
+    per-tensor scales; softmax_scale defaults to 1/sqrt(D); returns O [BH, Sq, D] of out_dtype."""
+    Q, K, V = _codes(Q), _codes(K), _codes(V)
+    _require(Q.dim() == 3 and K.dim() == 3 and V.dim() == 3, "Q, K, V must be [heads, seq, head_dim]")
+    BH, Sq, D = Q.shape
+    _require(K.shape == V.shape and K.shape[0] == BH and K.shape[2] == D, "K and V must be [heads, seq_kv, head_dim]")
+    _require(Q.is_contiguous() and K.is_contiguous() and V.is_contiguous(), "Q, K, V must be contiguous")
+    Skv = K.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(D) ** 0.5
+    code = _out_code(out_dtype)
+    O = _out_tensor(O, (BH, Sq, D), code, Q.device)
+    with torch.cuda.device(Q.device):
+        _check("fp8_attention", lib.fp8_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(scale_q), _ptr(scale_k), _ptr(scale_v),
+                                                  _ptr(O), BH, Sq, Skv, D, float(softmax_scale), int(bool(causal)),
+                                                  code, _stream(Q.device, stream)))
+    return O

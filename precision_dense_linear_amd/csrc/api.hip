@@ -336,6 +336,39 @@ fp8_status fp8_gemm_sparse24(const uint8_t* A, const uint8_t* Bv, const uint32_t
                     "fp8_gemm_sparse24");
 }
 
+fp8_status fp8_attention(const uint8_t* Q, const uint8_t* K, const uint8_t* V, const float* scale_q,
+                         const float* scale_k, const float* scale_v, void* O, int64_t batch_heads, int64_t seq_q,
+                         int64_t seq_kv, int64_t head_dim, float softmax_scale, int32_t causal, int32_t out_dtype,
+                         void* stream) {
+    if (batch_heads < 0 || seq_q < 0 || seq_kv < 0)
+        return fail(FP8_ERR_INVALID_ARG, "negative size (batch_heads=%lld seq_q=%lld seq_kv=%lld)",
+                    (long long)batch_heads, (long long)seq_q, (long long)seq_kv);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "head_dim=%lld is neither 64 nor 128", (long long)head_dim);
+    if (out_dtype != FP8_OUT_F32 && out_dtype != FP8_OUT_BF16 && out_dtype != FP8_OUT_F16)
+        return fail(FP8_ERR_INVALID_ARG, "out_dtype %#x is not FP8_OUT_F32, FP8_OUT_BF16 or FP8_OUT_F16", out_dtype);
+    if (causal != 0 && causal != 1) return fail(FP8_ERR_INVALID_ARG, "causal=%d is neither 0 nor 1", causal);
+    if (!(softmax_scale > 0.0f) || softmax_scale > 3.0e38f)
+        return fail(FP8_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
+    // one head's Q, K or V stays below 2^31 bytes (32-bit buffer offsets)
+    if (seq_q > (int64_t(1) << 31) / head_dim - 1 || seq_kv > (int64_t(1) << 31) / head_dim - 1)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "seq_q=%lld or seq_kv=%lld exceeds 2^31 / head_dim - 1",
+                    (long long)seq_q, (long long)seq_kv);
+    if (batch_heads * ((seq_q + 127) / 128) > (int64_t(1) << 31) - 1)
+        return fail(FP8_ERR_UNSUPPORTED_SHAPE, "too many query blocks");
+    const int64_t nq = batch_heads * seq_q;
+    const int64_t nkv = batch_heads * seq_kv;
+    if ((!Q && nq > 0) || ((!K || !V) && nkv > 0) || (!O && nq > 0))
+        return fail(FP8_ERR_INVALID_ARG, "null tensor pointer");
+    if (!scale_q || !scale_k || !scale_v) return fail(FP8_ERR_INVALID_ARG, "null scale pointer");
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+        return fail(FP8_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
+    if (nq == 0) return ok();
+    fp8k::AttnProblem g{Q, K, V, scale_q, scale_k, scale_v, O, batch_heads, seq_q, seq_kv, head_dim,
+                        softmax_scale, causal, out_dtype};
+    return from_hip(fp8k::launch_attention(g, (hipStream_t)stream), "fp8_attention");
+}
+
 fp8_status fp8_grouped_gemm(const uint8_t* A, const uint8_t* B, const int32_t* offsets, int32_t experts,
                             const float* scale_a, const float* scale_b, void* C, int64_t T, int64_t N, int64_t K,
                             int32_t out_dtype, void* stream) {

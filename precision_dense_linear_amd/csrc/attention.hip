@@ -1,0 +1,303 @@
+// FP8 multi-head attention for gfx950 ("Leveraging CUTLASS kernel naming in
+// Triton for a 100 TFLOPS FP8 tensor-core speed-up in multi-head attention":
+// the fp8_mha_kernel sketch -- Q K^T as an FP8 dot product, the softmax and
+// the accumulation of V fused behind it -- with BLOCK_M = 128 query rows and
+// BLOCK_N = 64 keys per step, its parameter list's values for a 4096-token,
+// 32-head LLM).  Per head h and query i:
+//
+//   S[i, j] = (scale_q * scale_k * softmax_scale) * sum_d Q[i, d] K[j, d]
+//   O[i, :] = scale_v * sum_j softmax_j(S[i, :]) V[j, :]
+//
+// over the visible keys (all, or causal: j <= i + seq_kv - seq_q).  Q, K, V
+// are E4M3 codes widened exactly to BF16 for the matrix cores, so both
+// products are exact and accumulate in FP32.  The softmax runs online over
+// 64-key blocks in FP32 (base-2 exponentials of the max-subtracted scores);
+// each unnormalised probability is rounded to BF16 for the second product
+// and the row sum adds the same rounded values; the output is divided by it
+// at the end.
+//
+// Layout: Q [BH][seq_q][D], K and V [BH][seq_kv][D], O [BH][seq_q][D], D
+// contiguous, D = 64 or 128.  A workgroup of 4 waves takes 128 queries of
+// one head; wave w owns queries 32w .. 32w+31 and walks every key block:
+//  * S^T = mfma(K fragment, Q fragment): lane l holds query l%32 and, per
+//    32-key block, the 16 keys 8(r/4) + 4(l/32) + r%4 (r = 0..15), so the
+//    row max and row sum of a query live in lanes l and l^32;
+//  * O^T = mfma(V fragment, P fragment): P comes straight from the S^T
+//    registers -- 16-key MFMA m of a 32-key block takes elements r = 8m ..
+//    8m+7, i.e. keys 16m + {0..3, 8..11} + 4(l/32) -- and V is staged in LDS
+//    with bits 2 and 3 of the key index swapped within each 16 rows, so the
+//    transposing LDS read (8 consecutive rows of one column) hands lane group
+//    g exactly those keys in that order;
+//  * O^T's register layout is the GEMM epilogue's (a lane owns one query and
+//    four consecutive d per group of four), so TileStore writes it.
+// K and V stages go from global memory straight into LDS (3 buffers, two
+// blocks of look-ahead).
+#include "gemm_common.h"
+#include "launch.h"
+
+namespace fp8k {
+
+namespace {
+
+constexpr int ATT_BM = 128;   // queries per workgroup
+constexpr int ATT_BN = 64;    // keys per step
+constexpr int ATT_NBUF = 3;   // K/V stage buffers
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct AttnArgs {
+    const uint8_t* Q;
+    const uint8_t* K;
+    const uint8_t* V;
+    const float* scale_q;
+    const float* scale_k;
+    const float* scale_v;
+    void* O;
+    int64_t seq_q, seq_kv;
+    float softmax_scale;
+    int32_t q_blocks;   // ceil(seq_q / 128)
+    int32_t causal;
+    int32_t out_f16;
+};
+
+// Chunk position of 16-byte chunk c of K-tile row r: rows sharing a 256-byte
+// bank window get distinct masks, so the 16 rows one ds_read_b128 phase reads
+// hit 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int r, int c) {
+    constexpr int RPW = 256 / D, CPR = D / 16;
+    return c ^ ((r / RPW) % CPR);
+}
+
+// V-tile row of key k (and key of row k): bits 2 and 3 swapped.
+__device__ __forceinline__ int v_row(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+template <int D, bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(256) attention_kernel(AttnArgs p) {
+    constexpr int TILE = ATT_BN * D;                // bytes of a K or V tile
+    constexpr int STAGE = 2 * TILE;
+    constexpr int DC = D / 32;                      // 32-wide d blocks; 16-byte chunks per lane group half
+    constexpr int LOADS = TILE / 1024 / 4;          // loads per wave per tile
+    using Store = TileStore<BF16, 1, DC>;
+    constexpr int EPI = 4 * Store::LDS_BYTES;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[ATT_NBUF * STAGE > EPI ? ATT_NBUF * STAGE : EPI];
+
+    int bid = blockIdx.x;
+    const int nblk = gridDim.x;
+    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);  // a head's query blocks on one XCD
+    const int head = bid / p.q_blocks;
+    const int qb = bid % p.q_blocks;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5;
+    const int64_t Sq = p.seq_q, Skv = p.seq_kv;
+    const int64_t q0 = (int64_t)qb * ATT_BM + wave * 32;      // this wave's first query
+    const int64_t my_q = q0 + (lane & 31);
+    const int64_t offs = Skv - Sq;                             // causal: key j visible to query i iff j <= i + offs
+
+    // key blocks this workgroup visits (causal: up to its last query's keys)
+    int64_t kv_end = Skv;
+    if constexpr (CAUSAL) {
+        const int64_t q_last = min<int64_t>((int64_t)qb * ATT_BM + ATT_BM - 1, Sq - 1);
+        kv_end = max<int64_t>(0, min<int64_t>(Skv, q_last + offs + 1));
+    }
+    const int nkb = (int)((kv_end + ATT_BN - 1) / ATT_BN);
+
+    const uint8_t* Kh = p.K + (int64_t)head * Skv * D;
+    const uint8_t* Vh = p.V + (int64_t)head * Skv * D;
+
+    // Q fragments: lane group g of the MFMA K slots takes d = (D/2) g + 8t ..
+    // +7 at step t (the d order is the contraction's own; K is read the same
+    // way), so a lane holds the D/2 contiguous bytes of its half of its row.
+    v8bf qf[D / 16];
+    {
+        v4i raw[DC];
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + (int64_t)head * Sq * D, clamp_records(Sq * D));
+        const uint32_t qoff = (uint32_t)(my_q * D + (D / 2) * h);
+#pragma unroll
+        for (int u = 0; u < DC; ++u)
+            raw[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, my_q < Sq ? qoff + 16 * u : OOB, 0, 0));
+#pragma unroll
+        for (int u = 0; u < DC; ++u) {
+            qf[2 * u] = e4m3x8_to_bf16(raw[u][0], raw[u][1]);
+            qf[2 * u + 1] = e4m3x8_to_bf16(raw[u][2], raw[u][3]);
+        }
+    }
+
+    // Per-lane global offsets (within a 64-key block) and LDS slots of this
+    // wave's stage loads: load i of K / V fills the 1 KiB slot (i*4 + wave).
+    uint32_t koff[LOADS], voff[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int o = (i * 4 + wave) * 1024 + lane * 16;
+        const int r = o / D, pos = (o % D) / 16;
+        koff[i] = (uint32_t)(r * D + (pos ^ (swz_k<D>(r, 0))) * 16);           // chunk c at position c ^ mask
+        const int vr = v_row(r);                                                 // key held by V-tile row r
+        voff[i] = (uint32_t)(vr * D + swz_b<D>(r, pos) * 16);                    // swz_b is its own inverse
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    auto issue = [&](int kb) {
+        const int64_t key0 = (int64_t)kb * ATT_BN;
+        const int buf = kb % ATT_NBUF;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + key0 * D, clamp_records((Skv - key0) * D));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + key0 * D, clamp_records((Skv - key0) * D));
+        const uint32_t base = lds0 + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            dma16(rk, __builtin_amdgcn_readfirstlane(base + (i * 4 + wave) * 1024), koff[i]);
+            dma16(rv, __builtin_amdgcn_readfirstlane(base + TILE + (i * 4 + wave) * 1024), voff[i]);
+        }
+    };
+
+    // LDS read offsets: K rows 32 kb + (l%32), chunk (D/32) g + u; V (mirror
+    // of the GEMM's B operand) rows 32 kb + 16 m + 8 g + (l%16)/2, column
+    // 32 ni + l%32 after the transpose.
+    int k_rd[2][DC];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < DC; ++u) {
+            const int r = kb * 32 + (lane & 31);
+            k_rd[kb][u] = r * D + swz_k<D>(r, DC * h + u) * 16;
+        }
+    int v_rd[2][2][DC];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int ni = 0; ni < DC; ++ni) {
+                const int col = ni * 32 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+                const int kr = kb * 32 + 16 * m + 8 * h + ((lane & 15) >> 1);
+                v_rd[kb][m][ni] = TILE + kr * D + swz_b<D>(kr, col >> 4) * 16 + (col & 15);
+            }
+
+    const float c2 = (p.scale_q[0] * p.scale_k[0]) * (p.softmax_scale * LOG2E);   // score -> log2 units
+    v16f acc[1][DC];
+#pragma unroll
+    for (int ni = 0; ni < DC; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][ni][r] = 0.0f;
+    float m_run = -__builtin_inff();
+    float l_run = 0.0f;   // this lane's share of the row sum (its 32 of every 64 keys)
+
+#pragma unroll
+    for (int kb = 0; kb < ATT_NBUF - 1; ++kb)
+        if (kb < nkb) issue(kb);
+
+    for (int kb = 0; kb < nkb; ++kb) {
+        // the loads of block kb have landed (block kb+1's may still fly),
+        // and every wave is done with the buffer block kb+2 refills
+        if (kb + 1 < nkb) wait_vmcnt_lds<2 * LOADS>();
+        else wait_vmcnt_lds<0>();
+        __syncthreads();
+        if (kb + ATT_NBUF - 1 < nkb) issue(kb + ATT_NBUF - 1);
+        const lds_u8* st = (const lds_u8*)smem + (kb % ATT_NBUF) * STAGE;
+
+        // S^T for the block's two 32-key halves
+        v16f s[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[hb][r] = 0.0f;
+#pragma unroll
+            for (int u = 0; u < DC; ++u) {
+                const v4i kr = lds_read16(st + k_rd[hb][u]);
+                s[hb] = mfma_32x32x16_bf16(e4m3x8_to_bf16(kr[0], kr[1]), qf[2 * u], s[hb]);
+                s[hb] = mfma_32x32x16_bf16(e4m3x8_to_bf16(kr[2], kr[3]), qf[2 * u + 1], s[hb]);
+            }
+        }
+        // scores in log2 units; keys past seq_kv (zero-filled) and, causal,
+        // past the query's last visible key are masked
+        const int64_t key0 = (int64_t)kb * ATT_BN;
+        const bool edge = key0 + ATT_BN > Skv || (CAUSAL && key0 + ATT_BN - 1 > q0 + offs);
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float v = s[hb][r] * c2;
+                if (edge) {
+                    const int64_t key = key0 + hb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool vis = key < Skv && (!CAUSAL || key <= my_q + offs);
+                    v = vis ? v : -__builtin_inff();
+                }
+                s[hb][r] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;   // no visible key yet
+        const float alpha = exp2f(m_run - m_use);
+        m_run = m_new;
+        // probabilities, rounded to BF16 for the second product; the row sum
+        // adds the same rounded values
+        v8bf pf[2][2];
+        float lsum = 0.0f;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const __bf16 b = (__bf16)exp2f(s[hb][8 * mm + e] - m_use);
+                    pf[hb][mm][e] = b;
+                    lsum += (float)b;
+                }
+        l_run = l_run * alpha + lsum;
+#pragma unroll
+        for (int ni = 0; ni < DC; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[0][ni][r] *= alpha;
+        // O^T += V^T P^T over the block's four 16-key groups
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int ni = 0; ni < DC; ++ni) {
+                    const v2i vr = lds_read_tr8(st + v_rd[hb][mm][ni]);
+                    acc[0][ni] = mfma_32x32x16_bf16(e4m3x8_to_bf16(vr[0], vr[1]), pf[hb][mm], acc[0][ni]);
+                }
+    }
+    wait_vmcnt<0>();
+
+    // O = scale_v * acc / l (0 for a query that saw no key)
+    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    __syncthreads();   // every wave is done with the stage buffers
+    lds_u8* scratch = (lds_u8*)smem + wave * Store::LDS_BYTES;
+    Store::run(p.O, acc, inv, p.scale_v[0], q0, 0, Sq, D, (int64_t)head * Sq, lane, scratch, p.out_f16 != 0);
+}
+
+template <int D, bool BF16>
+hipError_t launch_d(const AttnArgs& a, int64_t heads, hipStream_t s) {
+    const int64_t blocks = heads * a.q_blocks;
+    if (blocks == 0) return hipSuccess;
+    if (a.causal) hipLaunchKernelGGL((attention_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attention_kernel<D, BF16, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnProblem& g, hipStream_t s) {
+    AttnArgs a;
+    a.Q = g.Q;
+    a.K = g.K;
+    a.V = g.V;
+    a.scale_q = g.scale_q;
+    a.scale_k = g.scale_k;
+    a.scale_v = g.scale_v;
+    a.O = g.O;
+    a.seq_q = g.seq_q;
+    a.seq_kv = g.seq_kv;
+    a.softmax_scale = g.softmax_scale;
+    a.q_blocks = (int32_t)((g.seq_q + ATT_BM - 1) / ATT_BM);
+    a.causal = g.causal;
+    a.out_f16 = g.out == 2;
+    const bool two_byte = g.out != 0;
+    if (g.head_dim == 64) return two_byte ? launch_d<64, true>(a, g.heads, s) : launch_d<64, false>(a, g.heads, s);
+    return two_byte ? launch_d<128, true>(a, g.heads, s) : launch_d<128, false>(a, g.heads, s);
+}
+
+}  // namespace fp8k

@@ -71,4 +71,22 @@ hipError_t launch_quantize_2of4(const float* w, int64_t K, int64_t N, uint8_t* v
 hipError_t launch_gemm_blockscaled(const uint8_t* A, const uint8_t* B, const float* s_a, const float* s_b, void* C,
                                    int64_t M, int64_t N, int64_t K, int32_t out, int32_t block, hipStream_t s);
 
+// Multi-head attention on E4M3 Q, K, V (per-tensor scales): Q [heads][seq_q]
+// [head_dim], K and V [heads][seq_kv][head_dim], O [heads][seq_q][head_dim];
+// head_dim 64 or 128; out: 0 FP32, 1 BF16, 2 FP16.
+struct AttnProblem {
+    const uint8_t* Q;
+    const uint8_t* K;
+    const uint8_t* V;
+    const float* scale_q;
+    const float* scale_k;
+    const float* scale_v;
+    void* O;
+    int64_t heads, seq_q, seq_kv, head_dim;
+    float softmax_scale;
+    int32_t causal;
+    int32_t out;
+};
+hipError_t launch_attention(const AttnProblem& p, hipStream_t s);
+
 }  // namespace fp8k

@@ -20,6 +20,9 @@ motivate the FP8 GEMM with):
                          popularity (p_e proportional to (e+1)^-s, one i.i.d.
                          draw per token, rows grouped by expert), X (T x K)
                          N(0, 1), W (E x K x N) N(0, 0.02).
+* ``attention_qkv``   -- Q [heads, seq_q, D], K and V [heads, seq_kv, D],
+                         entries N(0, 1) (the attention page's LLM setting:
+                         32 heads, sequence 4096, head dimension 128).
 """
 from __future__ import annotations
 
@@ -102,3 +105,8 @@ def moe(E: int = 8, T: int = 16384, K: int = 4096, N: int = 14336, seed: int = 0
     for e in range(E):
         w[e] = gaussian((K, N), 0.02, seed, "moe-w%d" % e)
     return x, w, offsets_from_counts(counts)
+
+
+def attention_qkv(heads: int = 32, seq_q: int = 4096, seq_kv: int = 4096, D: int = 128, seed: int = 0):
+    return (gaussian((heads, seq_q, D), 1.0, seed, "Q"), gaussian((heads, seq_kv, D), 1.0, seed, "K"),
+            gaussian((heads, seq_kv, D), 1.0, seed, "V"))

@@ -1,0 +1,125 @@
+"""GPU parity of fp8_attention with the float64 oracle (oracle/attention.py),
+through the C ABI, on the same seeded inputs quantized per tensor on both
+sides.  Every output is held to the bound the header derives from the
+kernel's arithmetic (probabilities rounded to BF16: 2^-9 each, twice through
+the normalisation; FP32 accumulation over the keys; score errors of the FP32
+first product; one ulp of output rounding):
+
+    |O - O_exact| <= (1.01 (2^-8 + 4 dS) + 2^-23 (2 seq_kv + 16)) wabs
+                     + 2^-22 |O_exact| + ulp_out(|O_exact| + that)
+
+with wabs = scale_v * sum_j w_j |V[j, d]| and dS = 2^-24 (D max_j A + 6 max_j |S|)
+from the oracle.  Shapes: ragged query and key counts on both head
+dimensions, causal and not, all output types; the LLM shape (32 heads,
+sequence 4096, head dimension 128) on every output; decode (one query);
+queries without visible keys; no keys at all; equal scores (the mean of V)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as OA
+import precision_dense_linear_amd as P
+from parity import bf16_to_f64, bf16_ulp, f16_to_f64, f16_ulp, to_bits
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def quantized(shape, seed):
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+    q, s, _ = P.fp8_quantize(gpu(x))
+    oq, os_, _ = oracle.quantize_pertensor(x)
+    return q, s, oq, os_
+
+
+def check(O, Oex, wabs, sabs, smax, Skv, D, what):
+    if O.dtype == torch.float32:
+        got = O.cpu().numpy().astype(np.float64)
+        ulp = np.maximum(np.abs(Oex) * 2.0 ** -23, 2.0 ** -149)
+    elif O.dtype == torch.bfloat16:
+        got = bf16_to_f64(to_bits(O))
+        ulp = None
+    else:
+        got = f16_to_f64(to_bits(O))
+        ulp = None
+    dS = 2.0 ** -24 * (D * sabs + 6 * smax)[..., None]
+    f32 = (1.01 * (2.0 ** -8 + 4 * dS) + 2.0 ** -23 * (2 * Skv + 16)) * wabs + 2.0 ** -22 * np.abs(Oex)
+    at = np.abs(Oex) + f32
+    if ulp is None:
+        ulp = bf16_ulp(at) if O.dtype == torch.bfloat16 else f16_ulp(at)
+    bound = f32 + ulp
+    err = np.abs(got - Oex)
+    ratio = err / bound
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, ratio, 0)), err.shape)
+        raise AssertionError("%s: %d of %d outputs outside the bound; worst %s: got %r exact %r bound %r"
+                             % (what, int(bad.sum()), err.size, i, got[i], Oex[i], bound[i]))
+    rel = err / np.maximum(wabs, 1e-300)
+    print("%s: max err/bound %.3f, max err/wabs %.3g" % (what, ratio.max(), rel.max()), flush=True)
+
+
+def run_case(BH, Sq, Skv, D, causal, out, seed, scale=None):
+    q, sq, oq, osq = quantized((BH, Sq, D), seed)
+    k, sk, ok, osk = quantized((BH, Skv, D), seed + 1)
+    v, sv, ov, osv = quantized((BH, Skv, D), seed + 2)
+    ss = 1.0 / np.sqrt(D) if scale is None else scale
+    O = P.fp8_attention(q, k, v, sq, sk, sv, float(np.float32(ss)), causal, out)
+    torch.cuda.synchronize()
+    Oex, wabs, sabs, smax = OA.attention(oq, ok, ov, osq, osk, osv, float(np.float32(ss)), causal)
+    check(O, Oex, wabs, sabs, smax, Skv, D, "attention BH=%d Sq=%d Skv=%d D=%d causal=%s %s" % (
+        BH, Sq, Skv, D, causal, out))
+    return O
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Skv", [(200, 333), (128, 64), (77, 77), (300, 130)])
+def test_ragged_shapes(Sq, Skv, D, causal):
+    run_case(3, Sq, Skv, D, causal, torch.bfloat16, seed=Sq + Skv + D)
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.float16])
+def test_output_types(out):
+    run_case(2, 257, 513, 128, True, out, seed=7)
+    run_case(2, 190, 100, 64, False, out, seed=8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_llm_32_heads_4096_all_outputs(causal):
+    print("attention 32 x 4096 x 4096 x 128 causal=%s" % causal, flush=True)
+    O1 = run_case(32, 4096, 4096, 128, causal, torch.bfloat16, seed=11)
+    O2 = run_case(32, 4096, 4096, 128, causal, torch.bfloat16, seed=11)
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))      # deterministic
+
+
+def test_decode_one_query_and_long_keys():
+    run_case(8, 1, 4097, 128, False, torch.bfloat16, seed=21)
+    run_case(8, 1, 4097, 128, True, torch.float32, seed=22)
+
+
+def test_queries_without_keys_and_no_keys():
+    O = run_case(2, 100, 40, 64, True, torch.float32, seed=31)     # causal: the first 60 queries see no key
+    assert torch.count_nonzero(O[:, :60]).item() == 0
+    q, sq, _, _ = quantized((2, 50, 64), 32)
+    empty = torch.zeros((2, 0, 64), dtype=torch.uint8, device=DEV)
+    O = torch.full((2, 50, 64), float("nan"), device=DEV)
+    P.fp8_attention(q, empty, empty, sq, sq, sq, 0.125, False, torch.float32, O=O)
+    assert torch.count_nonzero(O).item() == 0
+
+
+def test_equal_scores_give_the_mean_of_v():
+    BH, Sq, Skv, D = 2, 130, 200, 128
+    q = torch.zeros((BH, Sq, D), dtype=torch.uint8, device=DEV)
+    one = torch.ones(1, device=DEV)
+    v, sv, ov, osv = quantized((BH, Skv, D), 41)
+    k, sk, _, _ = quantized((BH, Skv, D), 42)
+    O = P.fp8_attention(q, k, v, one, sk, sv, 0.1, False, torch.float32).cpu().numpy()
+    mean = oracle.decode(ov).mean(axis=1) * float(osv)            # every probability is exactly 1
+    assert np.allclose(O, np.broadcast_to(mean[:, None, :], O.shape), rtol=0,
+                       atol=2.0 ** -20 * float(np.abs(oracle.decode(ov)).max()) * float(osv))

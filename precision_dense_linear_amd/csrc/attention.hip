@@ -72,7 +72,7 @@ __device__ __forceinline__ int swz_k(int r, int c) {
 __device__ __forceinline__ int v_row(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 template <int D, bool BF16, bool CAUSAL>
-__global__ void __launch_bounds__(256) attention_kernel(AttnArgs p) {
+__global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
     constexpr int TILE = ATT_BN * D;                // bytes of a K or V tile
     constexpr int STAGE = 2 * TILE;
     constexpr int DC = D / 32;                      // 32-wide d blocks; 16-byte chunks per lane group half
@@ -227,7 +227,10 @@ __global__ void __launch_bounds__(256) attention_kernel(AttnArgs p) {
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;   // no visible key yet
-        const float alpha = exp2f(m_run - m_use);
+        // (v_exp_f32 itself: results below 2^-126, far under any weight
+        // that matters, flush to zero)
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        const bool rescale = __ballot(m_new != m_run) != 0;   // (alpha is exactly 1 where the max stayed)
         m_run = m_new;
         // probabilities, rounded to BF16 for the second product; the row sum
         // adds the same rounded values
@@ -239,15 +242,16 @@ __global__ void __launch_bounds__(256) attention_kernel(AttnArgs p) {
             for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const __bf16 b = (__bf16)exp2f(s[hb][8 * mm + e] - m_use);
+                    const __bf16 b = (__bf16)__builtin_amdgcn_exp2f(s[hb][8 * mm + e] - m_use);
                     pf[hb][mm][e] = b;
                     lsum += (float)b;
                 }
         l_run = l_run * alpha + lsum;
+        if (rescale)   // some query's running max moved (wave-uniform)
 #pragma unroll
-        for (int ni = 0; ni < DC; ++ni)
+            for (int ni = 0; ni < DC; ++ni)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[0][ni][r] *= alpha;
+                for (int r = 0; r < 16; ++r) acc[0][ni][r] *= alpha;
         // O^T += V^T P^T over the block's four 16-key groups
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)

@@ -16,6 +16,12 @@ int choose_splits(int64_t tiles, int64_t K, int per_cu, int64_t capacity);
 
 inline int64_t tiles_of(int64_t M, int64_t N, int BM, int BN) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
+// Plain GEMM with M <= 16 (gemm_skinny.hip): the split count it would use
+// (0 when the skinny class does not take the problem), and the launch.
+int skinny_splits(const GemmProblem& g);
+template <int FMT>
+hipError_t launch_skinny(const GemmProblem& g, hipStream_t s, int splits);
+
 template <int FMT, int BM, int BN, int WM, int WN, int KS, int NB, int GROUP_M>
 hipError_t launch_cfg(const GemmProblem& g, hipStream_t s) {
     return g.fast_acc ? launch_mode<BM, BN, WM, WN, KS, NB, GROUP_M, MODE_FAST, false, FMT>(g, s)
@@ -36,6 +42,11 @@ hipError_t launch_cfg_splitk(const GemmProblem& g, hipStream_t s, int32_t splits
 }
 
 // Tile configuration by shape class (a static table, no runtime tuning):
+//  * a plain GEMM with M <= 16 whose K the caller's workspace lets the
+//    skinny streaming kernel split (or that has enough 256-column tiles to
+//    fill half the CUs unsplit): that kernel (gemm_skinny.hip), in either
+//    accumulation mode -- reading B bounds it, so the exact products cost
+//    nothing over the FP8 rate;
 //  * M (rows per expert when grouped) <= 64: 32 x 64 tiles with each K step
 //    split over two wave groups -- many workgroups to stream B, HBM bound; a
 //    plain GEMM with fewer such tiles than half the GPU's workgroup slots
@@ -53,6 +64,10 @@ hipError_t launch_cfg_splitk(const GemmProblem& g, hipStream_t s, int32_t splits
 template <int FMT>
 hipError_t launch_gemm_t(const GemmProblem& g, hipStream_t s) {
     const bool plain = g.experts == 0;
+    if (plain && g.M <= 16) {
+        const int sk = skinny_splits(g);
+        if (sk > 0) return launch_skinny<FMT>(g, s, sk);
+    }
     const int64_t rows_per_problem = plain ? g.M : (g.M + g.experts - 1) / g.experts;
     // split_slots() is twice the CU count
     const bool few_mid_tiles = plain && tiles_of(g.M, g.N, 128, 128) * 4 < split_slots();

@@ -582,7 +582,8 @@ def main():
                 "basis": rotation,
                 "in_step_avg_kernel_us": round(avg_gemm_ms * 1e3, 2)}
     roof["kernel"] = {
-        "pertensor": "gemm_kernel (fp8_gemm)",
+        "pertensor": ("skinny_kernel (fp8_gemm with a workspace, M <= 16)" if getattr(w, "M", 1 << 30) <= 16
+                      else "gemm_kernel (fp8_gemm)"),
         "block": ("gemm_kernel MODE_BLOCK64 (fp8_gemm_blockscaled, 64x64 tiles)" if getattr(w, "block", 32) == 64
                   else "gemm_kernel MODE_BLOCK (fp8_gemm_blockscaled)"),
         "block_e8": "gemm_kernel MODE_E8M0 (fp8_gemm_blockscaled_e8m0)",

@@ -84,7 +84,10 @@ typedef enum fp8_out_dtype {
  * 2^max(e(acc)-30, E-24), floored, and rounded to nearest even.  Since
  * 2^E <= |a*b| for the group's largest product, the extra error per group
  * is below 7 * 2^-13 * max|a*b| (plus FP32-level terms); on N(0,1) data it
- * is ~1e-6 * sum_k |a*b| on average.
+ * is ~1e-6 * sum_k |a*b| on average.  The flag permits this accumulation
+ * and does not demand it: a plain GEMM with M <= 16 that runs the skinny
+ * class (see fp8_gemm_ws) is bound by reading B and computes the default
+ * mode's exact products at the same speed in either mode.
  */
 #define FP8_ACC_FAST 0x100
 
@@ -232,13 +235,19 @@ fp8_status fp8_gemm(const uint8_t* A, const uint8_t* B, const float* scale_a, co
  *   the partial sums at offset 0, then S arrival counters.  Every completed
  *   call leaves the counters at zero again (after a failed launch, zero the
  *   workspace before reusing it).
+ * M <= 16 (either accumulation mode): the skinny class splits K over up to
+ * 16 workgroups per 256-column tile, one workgroup per CU, each split
+ * taking 2 split tiles of the workspace (tiles x splits x 2 <= S); without
+ * room for a split it runs unsplit when there are at least half as many
+ * 256-column tiles as CUs, else the 32 x 64 class below takes the GEMM.
  * When the 32 x 64 tile class runs (M <= 64, or M <= 1024 with fewer
  * 128 x 128 tiles than half the GPU's CUs) and the output has too few
  * 32 x 64 tiles to fill the GPU, the K range is split over up to 8
- * workgroups per tile (tiles x splits <= S); each stores its FP32 partial
- * sums in the workspace and the last of a tile to finish adds them in split
- * order, so results are deterministic run to run (they may differ in the
- * last bits from fp8_gemm's unsplit sums, within the same bound).  Calls
+ * workgroups per tile (tiles x splits <= S).  In both, each split stores
+ * its FP32 partial sums in the workspace and the last of a tile to finish
+ * adds them in split order, so results are deterministic run to run (they
+ * may differ in the last bits from fp8_gemm's unsplit sums, within the
+ * same bound).  Calls
  * that share a workspace must not overlap in time (issue them on one
  * stream); graphs captured from such calls keep using the same workspace.
  */
@@ -254,7 +263,7 @@ fp8_status fp8_gemm_ws(const uint8_t* A, const uint8_t* B, const float* scale_a,
  * on, held until the process ends.  Same operation, arguments (less the
  * workspace), checks and errors as fp8_gemm_ws with a workspace of that
  * size, and bit-identical results.  The split count is chosen to fit the
- * array (tiles x splits <= 512), so no problem size needs more scratch than
+ * array (at most 512 split tiles), so no problem size needs more scratch than
  * it holds.  No allocation: the first call on a device looks up the array's
  * address there and clears its arrival counters with a kernel on `stream`
  * (FP8_ERR_HIP if that fails); every completed call leaves them at zero.

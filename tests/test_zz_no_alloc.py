@@ -25,11 +25,13 @@ def operands(M, N, K, seed):
     return (qa, qb, sa, sb), (a, b)
 
 
-# (first call, second call with a smaller input): 16 tiles x 8 splits then 8
-# tiles x 8; 64 tiles x 8 splits then 8 tiles x 2; an unsplit 128 x 128-tile
-# shape then a split 32 x 64 one
+# (first call, second call with a smaller input): 16 tiles of 32 x 64 x 8
+# splits then the skinny class (M <= 16: 256-column tiles) with 2 tiles x 8
+# splits; 64 tiles x 8 splits then skinny 2 tiles x 2; an unsplit
+# 128 x 128-tile shape then a split 32 x 64 one; skinny 32 tiles x 8 splits
+# (all 512 split tiles) then 4 tiles x 16 splits
 PAIRS = [((20, 1024, 8192), (16, 512, 4096)), ((64, 2048, 2304), (1, 512, 1024)),
-         ((300, 5648, 272), (40, 256, 1040))]
+         ((300, 5648, 272), (40, 256, 1040)), ((16, 8192, 8192), (3, 1024, 4112))]
 
 
 @pytest.mark.parametrize("first,second", PAIRS)

@@ -171,10 +171,15 @@ struct PipeCfg {
 // wave's LDS destination, lane l's 16 bytes land at M0 + 16*l.  The compiler
 // does not see these as LDS writes, so it neither serialises later LDS reads
 // behind them nor counts them; the kernel waits for them explicitly with
-// s_waitcnt vmcnt(n), n = loads issued after the stage it needs.  M0 is
-// listed as clobbered, which the compiler does not promise to honour for a
-// reserved register; that is safe only while no other code in these kernels
-// keeps a value in M0 (their gfx950 assembly has no other M0 access).
+// s_waitcnt vmcnt(n), n = loads issued after the stage it needs.  (The
+// compiler's own form, __builtin_amdgcn_raw_ptr_buffer_load_lds, makes it
+// wait for every such load before the next LDS read: 30 vmcnt(0) waits
+// instead of 2 in the 256 x 256 exact tile loop, which drains the pipeline.)
+// M0 is listed as clobbered, which the compiler does not promise to honour
+// for a reserved register; that is safe only while no other code in these
+// kernels keeps a value in M0.  tests/test_isa_invariants.py checks it on
+// every build: in the disassembly, each instruction naming M0 is this
+// s_mov_b32 directly followed by its LDS-direct load.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :

@@ -85,7 +85,9 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
     const int nblk = gridDim.x;
     if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);  // a head's query blocks on one XCD
     const int head = bid / p.q_blocks;
-    const int qb = bid % p.q_blocks;
+    // causal: a query block's work grows with its index, so the heaviest
+    // blocks of a head are issued first and the light ones fill in behind
+    const int qb = CAUSAL ? p.q_blocks - 1 - bid % p.q_blocks : bid % p.q_blocks;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5;

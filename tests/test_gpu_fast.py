@@ -68,7 +68,7 @@ def test_fast_workloads_within_bound(shape, out):
     print(shape, "max |err| / sum|ab| =", worst)
 
 
-@pytest.mark.parametrize("M,N", [(16, 8192), (4096, 28672)])
+@pytest.mark.parametrize("M,N", [(16, 8192), (128, 28672), (4096, 28672)])
 def test_fast_llm_within_bound(M, N):
     a, w = W.llm_linear(M, N, 8192)
     qa, sa, _ = P.fp8_quantize(gpu(a))

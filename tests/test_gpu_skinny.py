@@ -1,7 +1,7 @@
 """The skinny GEMM class (plain GEMM, M <= 16 rows) through the C ABI: bit
 for bit on small-integer codes (every partial sum exact in FP32, so any
 order gives the oracle's value) over ragged M, N and K (K ending inside a
-32-byte stage and inside a 16-byte chunk), both FP8 formats per operand,
+32-byte stage; K is a multiple of 16), both FP8 formats per operand,
 every output type, in both accumulation modes, with K split across 2 to 16
 workgroups (fp8_gemm_ws, two workspace sizes) and unsplit (enough column
 tiles, a ragged last one); random end-to-end cases within the FP32 / BF16

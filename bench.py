@@ -95,19 +95,23 @@ class SclkSampler:
         return float(np.mean(busy)) if busy else None
 
 
-def csrc_sha256():
-    import glob
+# The sources the 8192^3 per-tensor GEMM kernel is compiled from: its
+# committed byte counters stay valid while these are unchanged.
+HEADLINE_SOURCES = ("device_utils.h", "gemm_common.h", "gemm_kernel.h", "gemm_dispatch.h", "launch.h", "gemm.hip")
+
+
+def csrc_sha256(names=HEADLINE_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "precision_dense_linear_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+    for n in sorted(names):
+        h.update(n.encode())
+        h.update(open(os.path.join(ROOT, "precision_dense_linear_amd", "csrc", n), "rb").read())
     return h.hexdigest()
 
 
 def measured_traffic(workload):
     """HBM bytes per GEMM launch from the committed rocprofv3 byte counters, if
-    they were taken on the kernel sources as they are now (else None)."""
+    they were taken on the kernel's sources as they are now (else None)."""
     path = os.path.join(PROFILES, {"gemm8192": "gemm_kernel_8192x8192x8192_bf16.traffic.json"}.get(workload, "-"))
     if not os.path.exists(path):
         return None

@@ -455,11 +455,15 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     // layout, coalesced; rows past M skipped) and counts itself in; the last
     // to arrive sums all the tile's partials in split order -- the same order
     // whichever split is last, so the result is deterministic -- and writes
-    // C.  Partials are stored and loaded as device-scope atomics (coherent
-    // across the XCDs' L2s); the arrival count is an acquire-release
-    // read-modify-write at device scope, so each split's partial stores
-    // happen before its count, and the count the last split reads happens
-    // before its loads of the partials.  No workgroup ever waits on another.
+    // C.  Partials, counters and the last split's reads are relaxed
+    // device-scope atomics: on gfx950 loads and stores that bypass the
+    // non-coherent cache levels (coherent across the XCDs' L2s).  A split
+    // counts itself in only after its partial stores have completed (vmcnt
+    // 0, then a barrier for the other waves' stores), and the last split
+    // reads the partials only after its count has returned; this ordering
+    // rests on that cache behaviour rather than on release/acquire, whose
+    // whole-L2 write-back and invalidate per workgroup measured 23.8 ->
+    // 40.7 us at M = 16, N = K = 8192.  No workgroup ever waits on another.
     // (With KS > 1 only wave group 0 holds the tile's sums; the other groups
     // take part in the barriers and leave before the epilogue.)
     if constexpr (SPLITK) {

@@ -29,7 +29,9 @@ constexpr int SK_BN = 256;                // columns per workgroup
 constexpr int SK_KS = 32;                 // K bytes per stage
 constexpr int SK_W = 8;                   // waves per workgroup
 constexpr int SK_NI = SK_BN / SK_W / 16;  // 16-column MFMA blocks per wave
-constexpr int SK_A = 1024;                // A part of a stage: 16 rows x 32 bytes (+ 512 zero)
+constexpr int SK_T = SK_KS / 32;          // 32-deep MFMA steps per stage
+constexpr int SK_CA = SK_KS / 16;         // 16-byte chunks per A row of a stage
+constexpr int SK_A = 1024;                // A part of a stage: 16 rows x SK_KS bytes (the rest zero)
 constexpr int SK_STAGE = SK_A + SK_KS * SK_BN;
 constexpr int SK_CHUNK = 8;               // partials read at a time by the last split
 constexpr int SK_SLOTS = SK_BN * 16 / SPLIT_TILE_FLOATS;  // workspace split tiles per partial
@@ -42,9 +44,10 @@ __device__ __forceinline__ v4f_t mfma_16x16x32_bf16(v8bf a, v8bf b, v4f_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// A part layout: row m's 16-byte chunk c (of 2) at position c ^ ((m >> 3) & 1),
-// so the 8-byte reads of rows m and m + 8 fall in different banks.
-__device__ __forceinline__ int swz_sa(int m, int c) { return c ^ ((m >> 3) & 1); }
+// A part layout: row m's 16-byte chunk c (of SK_CA) at position
+// c ^ ((m / (16 / SK_CA)) % SK_CA), so the 8-byte reads of rows 0..15 at one
+// chunk fall in distinct banks.
+__device__ __forceinline__ int swz_sa(int m, int c) { return c ^ ((m / (16 / SK_CA)) % SK_CA); }
 
 template <int R, bool BF16, bool SPLITK, int FMT>
 __global__ void __launch_bounds__(64 * SK_W) skinny_kernel(GemmArgs p) {
@@ -79,8 +82,8 @@ __global__ void __launch_bounds__(64 * SK_W) skinny_kernel(GemmArgs p) {
         const int br = 4 * (SK_LPW * wave + i) + (lane >> 4), bc = swz_b<SK_BN>(br, lane & 15);
         b_off[i] = n0 + bc * 16 < N ? (uint32_t)(br * N + bc * 16) : OOB;
     }
-    const int am = (lane & 31) >> 1, ac = swz_sa(am, lane & 1);
-    const bool a_lane_ok = lane < 32 && am < M;
+    const int am = lane / SK_CA, ac = swz_sa(am, lane % SK_CA);
+    const bool a_lane_ok = lane < 16 * SK_CA && am < M;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, clamp_records(M * K));
     auto issue = [&](int j) {
@@ -99,17 +102,21 @@ __global__ void __launch_bounds__(64 * SK_W) skinny_kernel(GemmArgs p) {
         }
     };
 
-    // LDS read offsets within a stage: A -- lane (g, m = l%16) reads K
-    // 8 g .. +7 of row m; B -- this wave's 16-column block h: rows
-    // 8 g + (l%16)/2, columns 32 w + 16 h + 8 (l&1) (transposed on read: lane
-    // (g, i) gets column 32 w + 16 h + i, K rows 8 g .. +7)
-    const int a_rd = i16 * 32 + swz_sa(i16, g >> 1) * 16 + 8 * (g & 1);
-    int b_rd[SK_NI];
+    // LDS read offsets within a stage, per 32-deep step t: A -- lane (g,
+    // m = l%16) reads K 32 t + 8 g .. +7 of row m; B -- this wave's
+    // 16-column block h: rows 32 t + 8 g + (l%16)/2, columns 32 w + 16 h +
+    // 8 (l&1) (transposed on read: lane (g, i) gets column 32 w + 16 h + i,
+    // K rows 32 t + 8 g .. +7)
+    int a_rd[SK_T], b_rd[SK_T][SK_NI];
 #pragma unroll
-    for (int h = 0; h < SK_NI; ++h) {
-        const int r = 8 * g + (i16 >> 1);
-        const int col = SK_NI * 16 * wave + 16 * h + 8 * (i16 & 1);
-        b_rd[h] = SK_A + r * SK_BN + swz_b<SK_BN>(r, col >> 4) * 16 + (col & 15);
+    for (int t = 0; t < SK_T; ++t) {
+        a_rd[t] = i16 * SK_KS + swz_sa(i16, 2 * t + (g >> 1)) * 16 + 8 * (g & 1);
+#pragma unroll
+        for (int h = 0; h < SK_NI; ++h) {
+            const int r = 32 * t + 8 * g + (i16 >> 1);
+            const int col = SK_NI * 16 * wave + 16 * h + 8 * (i16 & 1);
+            b_rd[t][h] = SK_A + r * SK_BN + swz_b<SK_BN>(r, col >> 4) * 16 + (col & 15);
+        }
     }
 
     v4f_t acc[SK_NI];
@@ -127,12 +134,15 @@ __global__ void __launch_bounds__(64 * SK_W) skinny_kernel(GemmArgs p) {
         __syncthreads();
         issue(j + R - 1);
         const lds_u8* e = (const lds_u8*)smem + (j % R) * SK_STAGE;
-        const v2i av = *(const __attribute__((address_space(3))) v2i*)(e + a_rd);
-        const v8bf af = fp8x8_to_bf16<FA>(av[0], av[1]);
 #pragma unroll
-        for (int h = 0; h < SK_NI; ++h) {
-            const v2i bv = lds_read_tr8(e + b_rd[h]);
-            acc[h] = mfma_16x16x32_bf16(fp8x8_to_bf16<FB>(bv[0], bv[1]), af, acc[h]);
+        for (int t = 0; t < SK_T; ++t) {
+            const v2i av = *(const __attribute__((address_space(3))) v2i*)(e + a_rd[t]);
+            const v8bf af = fp8x8_to_bf16<FA>(av[0], av[1]);
+#pragma unroll
+            for (int h = 0; h < SK_NI; ++h) {
+                const v2i bv = lds_read_tr8(e + b_rd[t][h]);
+                acc[h] = mfma_16x16x32_bf16(fp8x8_to_bf16<FB>(bv[0], bv[1]), af, acc[h]);
+            }
         }
     }
     wait_vmcnt<0>();                        // (the empty loads past the last stage)

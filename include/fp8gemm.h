@@ -380,7 +380,8 @@ fp8_status fp8_grouped_gemm(const uint8_t* A, const uint8_t* B, const int32_t* o
  * j <= i + seq_kv - seq_q; a query that sees no key gets O = 0.
  * Q: batch_heads x seq_q x head_dim E4M3 codes, K and V: batch_heads x
  * seq_kv x head_dim, O: batch_heads x seq_q x head_dim of out_dtype
- * (FP8_OUT_F32, _BF16 or _F16, no flags); all row-major, head_dim
+ * (FP8_OUT_F32, _BF16 or _F16, optionally OR-ed with FP8_ACC_FAST, below;
+ * no other flag); all row-major, head_dim
  * contiguous, 16-byte aligned.  scale_q, scale_k, scale_v: one float each on
  * the device (as fp8_quantize writes them); softmax_scale on the host,
  * positive and finite (1/sqrt(head_dim) for standard attention).
@@ -393,6 +394,13 @@ fp8_status fp8_grouped_gemm(const uint8_t* A, const uint8_t* B, const int32_t* o
  *     + 2^-22 |O_exact| + 1 ulp of the output type at |O_exact| + that bound,
  * dS = 2^-24 * (head_dim * max_j A[i, j] + 6 max_j |S[i, j]|), A the score
  * with every product taken in magnitude (max over the visible keys).
+ * With FP8_ACC_FAST, Q K^T runs on the FP8 matrix cores (the page's FP8 dot
+ * product; twice the rate, no widening of Q and K), accumulating as the
+ * GEMM's FP8_ACC_FAST does (groups of 8 consecutive d aligned to their
+ * largest product and truncated to 13 bits below it); the rest is
+ * unchanged, and the same bound holds with
+ * dS = (7 * 2^-13 + 2^-21) * max_j A[i, j] + 2^-24 * (head_dim * max_j A[i, j] + 6 max_j |S[i, j]|)
+ * while that dS stays below 0.6 (e^(2 dS) - 1 <= 4 dS).
  * batch_heads, seq_q, seq_kv >= 0; head_dim 64 or 128 (else
  * FP8_ERR_UNSUPPORTED_SHAPE); seq_q, seq_kv < 2^31 / head_dim.
  */

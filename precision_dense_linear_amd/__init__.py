@@ -392,9 +392,10 @@ def fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype=torch.bfloat16, 
 
 
 def fp8_attention(Q, K, V, scale_q, scale_k, scale_v, softmax_scale=None, causal=False, out_dtype=torch.bfloat16,
-                  O=None, stream=None):
+                  O=None, stream=None, fast=False):
     """Multi-head attention on E4M3 codes: Q [BH, Sq, D], K and V [BH, Skv, D] (D = 64 or 128),
-    per-tensor scales; softmax_scale defaults to 1/sqrt(D); returns O [BH, Sq, D] of out_dtype."""
+    per-tensor scales; softmax_scale defaults to 1/sqrt(D); returns O [BH, Sq, D] of out_dtype.
+    fast=True computes Q K^T on the FP8 matrix cores (FP8_ACC_FAST)."""
     Q, K, V = _codes(Q), _codes(K), _codes(V)
     _require(Q.dim() == 3 and K.dim() == 3 and V.dim() == 3, "Q, K, V must be [heads, seq, head_dim]")
     BH, Sq, D = Q.shape
@@ -408,5 +409,5 @@ def fp8_attention(Q, K, V, scale_q, scale_k, scale_v, softmax_scale=None, causal
     with torch.cuda.device(Q.device):
         _check("fp8_attention", lib.fp8_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(scale_q), _ptr(scale_k), _ptr(scale_v),
                                                   _ptr(O), BH, Sq, Skv, D, float(softmax_scale), int(bool(causal)),
-                                                  code, _stream(Q.device, stream)))
+                                                  code | (FP8_ACC_FAST if fast else 0), _stream(Q.device, stream)))
     return O

@@ -345,8 +345,12 @@ fp8_status fp8_attention(const uint8_t* Q, const uint8_t* K, const uint8_t* V, c
                     (long long)batch_heads, (long long)seq_q, (long long)seq_kv);
     if (head_dim != 64 && head_dim != 128)
         return fail(FP8_ERR_UNSUPPORTED_SHAPE, "head_dim=%lld is neither 64 nor 128", (long long)head_dim);
-    if (out_dtype != FP8_OUT_F32 && out_dtype != FP8_OUT_BF16 && out_dtype != FP8_OUT_F16)
-        return fail(FP8_ERR_INVALID_ARG, "out_dtype %#x is not FP8_OUT_F32, FP8_OUT_BF16 or FP8_OUT_F16", out_dtype);
+    const bool fast_qk = (out_dtype & FP8_ACC_FAST) != 0;
+    const int32_t out_kind = out_dtype & ~FP8_ACC_FAST;
+    if (out_kind != FP8_OUT_F32 && out_kind != FP8_OUT_BF16 && out_kind != FP8_OUT_F16)
+        return fail(FP8_ERR_INVALID_ARG,
+                    "out_dtype %#x is not FP8_OUT_F32, FP8_OUT_BF16 or FP8_OUT_F16 (optionally with FP8_ACC_FAST)",
+                    out_dtype);
     if (causal != 0 && causal != 1) return fail(FP8_ERR_INVALID_ARG, "causal=%d is neither 0 nor 1", causal);
     if (!(softmax_scale > 0.0f) || softmax_scale > 3.0e38f)
         return fail(FP8_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
@@ -365,7 +369,7 @@ fp8_status fp8_attention(const uint8_t* Q, const uint8_t* K, const uint8_t* V, c
         return fail(FP8_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
     if (nq == 0) return ok();
     fp8k::AttnProblem g{Q, K, V, scale_q, scale_k, scale_v, O, batch_heads, seq_q, seq_kv, head_dim,
-                        softmax_scale, causal, out_dtype};
+                        softmax_scale, causal, out_kind, fast_qk};
     return from_hip(fp8k::launch_attention(g, (hipStream_t)stream), "fp8_attention");
 }
 

@@ -71,7 +71,7 @@ __device__ __forceinline__ int swz_k(int r, int c) {
 // V-tile row of key k (and key of row k): bits 2 and 3 swapped.
 __device__ __forceinline__ int v_row(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool FASTQK>
 __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
     constexpr int TILE = ATT_BN * D;                // bytes of a K or V tile
     constexpr int STAGE = 2 * TILE;
@@ -110,8 +110,20 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
     // Q fragments: lane group g of the MFMA K slots takes d = (D/2) g + 8t ..
     // +7 at step t (the d order is the contraction's own; K is read the same
     // way), so a lane holds the D/2 contiguous bytes of its half of its row.
-    v8bf qf[D / 16];
-    {
+    // FASTQK: instruction m (K = 64) of a 32-key block takes d = 64 m + 32 g
+    // .. +31 from lane group g, as raw codes (K read the same way).
+    v8bf qf[FASTQK ? 1 : D / 16];
+    v8i q8[D / 64];
+    if constexpr (FASTQK) {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + (int64_t)head * Sq * D, clamp_records(Sq * D));
+#pragma unroll
+        for (int m = 0; m < D / 64; ++m) {
+            const uint32_t o = (uint32_t)(my_q * D + 64 * m + 32 * h);
+            const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, my_q < Sq ? o : OOB, 0, 0));
+            const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, my_q < Sq ? o + 16 : OOB, 0, 0));
+            q8[m] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    } else {
         v4i raw[DC];
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + (int64_t)head * Sq * D, clamp_records(Sq * D));
         const uint32_t qoff = (uint32_t)(my_q * D + (D / 2) * h);
@@ -153,13 +165,16 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
     // LDS read offsets: K rows 32 kb + (l%32), chunk (D/32) g + u; V (mirror
     // of the GEMM's B operand) rows 32 kb + 16 m + 8 g + (l%16)/2, column
     // 32 ni + l%32 after the transpose.
+    // (FASTQK: K rows 32 kb + (l%32), chunks 4 m + 2 g and 4 m + 2 g + 1 for
+    // instruction m, the same d as the lane's Q bytes)
     int k_rd[2][DC];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int u = 0; u < DC; ++u) {
             const int r = kb * 32 + (lane & 31);
-            k_rd[kb][u] = r * D + swz_k<D>(r, DC * h + u) * 16;
+            const int c = FASTQK ? 4 * (u / 2) + 2 * h + (u % 2) : DC * h + u;
+            k_rd[kb][u] = r * D + swz_k<D>(r, c) * 16;
         }
     int v_rd[2][2][DC];
 #pragma unroll
@@ -201,11 +216,20 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
         for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[hb][r] = 0.0f;
+            if constexpr (FASTQK) {
 #pragma unroll
-            for (int u = 0; u < DC; ++u) {
-                const v4i kr = lds_read16(st + k_rd[hb][u]);
-                s[hb] = mfma_32x32x16_bf16(e4m3x8_to_bf16(kr[0], kr[1]), qf[2 * u], s[hb]);
-                s[hb] = mfma_32x32x16_bf16(e4m3x8_to_bf16(kr[2], kr[3]), qf[2 * u + 1], s[hb]);
+                for (int m = 0; m < D / 64; ++m) {
+                    const v4i lo = lds_read16(st + k_rd[hb][2 * m]), hi = lds_read16(st + k_rd[hb][2 * m + 1]);
+                    const v8i k8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    s[hb] = mfma_32x32x64_f8<0, 0>(k8, q8[m], s[hb]);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < DC; ++u) {
+                    const v4i kr = lds_read16(st + k_rd[hb][u]);
+                    s[hb] = mfma_32x32x16_bf16(e4m3x8_to_bf16(kr[0], kr[1]), qf[2 * u], s[hb]);
+                    s[hb] = mfma_32x32x16_bf16(e4m3x8_to_bf16(kr[2], kr[3]), qf[2 * u + 1], s[hb]);
+                }
             }
         }
         // scores in log2 units; keys past seq_kv (zero-filled) and, causal,
@@ -275,13 +299,21 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
     Store::run(p.O, acc, inv, p.scale_v[0], q0, 0, Sq, D, (int64_t)head * Sq, lane, scratch, p.out_f16 != 0);
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool FASTQK>
 hipError_t launch_d(const AttnArgs& a, int64_t heads, hipStream_t s) {
     const int64_t blocks = heads * a.q_blocks;
     if (blocks == 0) return hipSuccess;
-    if (a.causal) hipLaunchKernelGGL((attention_kernel<D, BF16, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attention_kernel<D, BF16, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    if (a.causal)
+        hipLaunchKernelGGL((attention_kernel<D, BF16, true, FASTQK>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attention_kernel<D, BF16, false, FASTQK>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     return hipGetLastError();
+}
+
+template <bool FASTQK>
+hipError_t launch_fast(const AttnArgs& a, int64_t heads, int64_t head_dim, bool two_byte, hipStream_t s) {
+    if (head_dim == 64)
+        return two_byte ? launch_d<64, true, FASTQK>(a, heads, s) : launch_d<64, false, FASTQK>(a, heads, s);
+    return two_byte ? launch_d<128, true, FASTQK>(a, heads, s) : launch_d<128, false, FASTQK>(a, heads, s);
 }
 
 }  // namespace
@@ -302,8 +334,8 @@ hipError_t launch_attention(const AttnProblem& g, hipStream_t s) {
     a.causal = g.causal;
     a.out_f16 = g.out == 2;
     const bool two_byte = g.out != 0;
-    if (g.head_dim == 64) return two_byte ? launch_d<64, true>(a, g.heads, s) : launch_d<64, false>(a, g.heads, s);
-    return two_byte ? launch_d<128, true>(a, g.heads, s) : launch_d<128, false>(a, g.heads, s);
+    return g.fast_qk ? launch_fast<true>(a, g.heads, g.head_dim, two_byte, s)
+                     : launch_fast<false>(a, g.heads, g.head_dim, two_byte, s);
 }
 
 }  // namespace fp8k

@@ -86,6 +86,7 @@ struct AttnProblem {
     float softmax_scale;
     int32_t causal;
     int32_t out;
+    bool fast_qk;   // Q K^T on the FP8 matrix cores (FP8_ACC_FAST)
 };
 hipError_t launch_attention(const AttnProblem& p, hipStream_t s);
 

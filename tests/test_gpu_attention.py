@@ -9,7 +9,9 @@ first product; one ulp of output rounding):
                      + 2^-22 |O_exact| + ulp_out(|O_exact| + that)
 
 with wabs = scale_v * sum_j w_j |V[j, d]| and dS = 2^-24 (D max_j A + 6 max_j |S|)
-from the oracle.  Shapes: ragged query and key counts on both head
+from the oracle; with Q K^T on the FP8 matrix cores (fast=True) dS grows by
+(7 * 2^-13 + 2^-21) max_j A, the FP8_ACC_FAST truncation per group of 8
+products.  Shapes: ragged query and key counts on both head
 dimensions, causal and not, all output types; the LLM shape (32 heads,
 sequence 4096, head dimension 128) on every output; decode (one query);
 queries without visible keys; no keys at all; equal scores (the mean of V)."""
@@ -37,7 +39,7 @@ def quantized(shape, seed):
     return q, s, oq, os_
 
 
-def check(O, Oex, wabs, sabs, smax, Skv, D, what):
+def check(O, Oex, wabs, sabs, smax, Skv, D, what, fast=False):
     if O.dtype == torch.float32:
         got = O.cpu().numpy().astype(np.float64)
         ulp = np.maximum(np.abs(Oex) * 2.0 ** -23, 2.0 ** -149)
@@ -48,6 +50,9 @@ def check(O, Oex, wabs, sabs, smax, Skv, D, what):
         got = f16_to_f64(to_bits(O))
         ulp = None
     dS = 2.0 ** -24 * (D * sabs + 6 * smax)[..., None]
+    if fast:    # Q K^T on the FP8 matrix cores: the FP8_ACC_FAST truncation per group of 8 products
+        dS = dS + (7 * 2.0 ** -13 + 2.0 ** -21) * sabs[..., None]
+        assert dS.max() < 0.6, "the bound's linearisation needs dS < 0.6 (max %g)" % dS.max()
     f32 = (1.01 * (2.0 ** -8 + 4 * dS) + 2.0 ** -23 * (2 * Skv + 16)) * wabs + 2.0 ** -22 * np.abs(Oex)
     at = np.abs(Oex) + f32
     if ulp is None:
@@ -64,43 +69,47 @@ def check(O, Oex, wabs, sabs, smax, Skv, D, what):
     print("%s: max err/bound %.3f, max err/wabs %.3g" % (what, ratio.max(), rel.max()), flush=True)
 
 
-def run_case(BH, Sq, Skv, D, causal, out, seed, scale=None):
+def run_case(BH, Sq, Skv, D, causal, out, seed, scale=None, fast=False):
     q, sq, oq, osq = quantized((BH, Sq, D), seed)
     k, sk, ok, osk = quantized((BH, Skv, D), seed + 1)
     v, sv, ov, osv = quantized((BH, Skv, D), seed + 2)
     ss = 1.0 / np.sqrt(D) if scale is None else scale
-    O = P.fp8_attention(q, k, v, sq, sk, sv, float(np.float32(ss)), causal, out)
+    O = P.fp8_attention(q, k, v, sq, sk, sv, float(np.float32(ss)), causal, out, fast=fast)
     torch.cuda.synchronize()
     Oex, wabs, sabs, smax = OA.attention(oq, ok, ov, osq, osk, osv, float(np.float32(ss)), causal)
-    check(O, Oex, wabs, sabs, smax, Skv, D, "attention BH=%d Sq=%d Skv=%d D=%d causal=%s %s" % (
-        BH, Sq, Skv, D, causal, out))
+    check(O, Oex, wabs, sabs, smax, Skv, D, "attention BH=%d Sq=%d Skv=%d D=%d causal=%s %s fast=%s" % (
+        BH, Sq, Skv, D, causal, out, fast), fast=fast)
     return O
 
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Sq,Skv", [(200, 333), (128, 64), (77, 77), (300, 130)])
-def test_ragged_shapes(Sq, Skv, D, causal):
-    run_case(3, Sq, Skv, D, causal, torch.bfloat16, seed=Sq + Skv + D)
+@pytest.mark.parametrize("fast", [False, True])
+def test_ragged_shapes(Sq, Skv, D, causal, fast):
+    run_case(3, Sq, Skv, D, causal, torch.bfloat16, seed=Sq + Skv + D, fast=fast)
 
 
 @pytest.mark.parametrize("out", [torch.float32, torch.float16])
-def test_output_types(out):
-    run_case(2, 257, 513, 128, True, out, seed=7)
-    run_case(2, 190, 100, 64, False, out, seed=8)
+@pytest.mark.parametrize("fast", [False, True])
+def test_output_types(out, fast):
+    run_case(2, 257, 513, 128, True, out, seed=7, fast=fast)
+    run_case(2, 190, 100, 64, False, out, seed=8, fast=fast)
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_llm_32_heads_4096_all_outputs(causal):
-    print("attention 32 x 4096 x 4096 x 128 causal=%s" % causal, flush=True)
-    O1 = run_case(32, 4096, 4096, 128, causal, torch.bfloat16, seed=11)
-    O2 = run_case(32, 4096, 4096, 128, causal, torch.bfloat16, seed=11)
+@pytest.mark.parametrize("fast", [False, True])
+def test_llm_32_heads_4096_all_outputs(causal, fast):
+    print("attention 32 x 4096 x 4096 x 128 causal=%s fast=%s" % (causal, fast), flush=True)
+    O1 = run_case(32, 4096, 4096, 128, causal, torch.bfloat16, seed=11, fast=fast)
+    O2 = run_case(32, 4096, 4096, 128, causal, torch.bfloat16, seed=11, fast=fast)
     assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))      # deterministic
 
 
 def test_decode_one_query_and_long_keys():
     run_case(8, 1, 4097, 128, False, torch.bfloat16, seed=21)
     run_case(8, 1, 4097, 128, True, torch.float32, seed=22)
+    run_case(8, 1, 4097, 128, True, torch.float32, seed=23, fast=True)
 
 
 def test_queries_without_keys_and_no_keys():

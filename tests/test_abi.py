@@ -223,3 +223,39 @@ def test_missing_library_fails_loudly(tmp_path):
             "else:\n    print('IMPORTED', precision_dense_linear_amd.__file__)\n") % str(tmp_path)
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300).stdout
     assert "IMPORT-ERROR" in out and "not built" in out, out
+
+
+def attention(Q=FAKE, K=FAKE, V=FAKE, sq=FAKE, sk=FAKE, sv=FAKE, O=FAKE, BH=2, Sq=64, Skv=64, D=128, scale=0.125,
+              causal=0, out=1):
+    return P.lib.fp8_attention(Q, K, V, sq, sk, sv, O, BH, Sq, Skv, D, scale, causal, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), P.FP8_ERR_UNSUPPORTED_SHAPE),
+    (dict(D=256), P.FP8_ERR_UNSUPPORTED_SHAPE),
+    (dict(BH=-1), P.FP8_ERR_INVALID_ARG),
+    (dict(Sq=-1), P.FP8_ERR_INVALID_ARG),
+    (dict(out=3), P.FP8_ERR_INVALID_ARG),
+    (dict(out=1 | 0x200), P.FP8_ERR_INVALID_ARG),              # operand formats: not taken here
+    (dict(out=1 | 0x800), P.FP8_ERR_INVALID_ARG),
+    (dict(out=1 | 0x100, Sq=0), P.FP8_OK),                     # FP8_ACC_FAST: accepted
+    (dict(causal=2), P.FP8_ERR_INVALID_ARG),
+    (dict(scale=0.0), P.FP8_ERR_INVALID_ARG),
+    (dict(scale=-1.0), P.FP8_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), P.FP8_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), P.FP8_ERR_INVALID_ARG),
+    (dict(Q=None), P.FP8_ERR_INVALID_ARG),
+    (dict(K=None), P.FP8_ERR_INVALID_ARG),
+    (dict(O=None), P.FP8_ERR_INVALID_ARG),
+    (dict(sv=None), P.FP8_ERR_INVALID_ARG),
+    (dict(V=FAKE_ODD), P.FP8_ERR_INVALID_ARG),
+    (dict(Sq=1 << 24), P.FP8_ERR_UNSUPPORTED_SHAPE),           # one head past 2^31 bytes
+    (dict(Skv=1 << 25, D=64), P.FP8_ERR_UNSUPPORTED_SHAPE),
+    (dict(Sq=0), P.FP8_OK),                                    # nothing to write
+    (dict(BH=0), P.FP8_OK),
+    (dict(K=None, V=None, Skv=0, Sq=0), P.FP8_OK),
+])
+def test_attention_validation(kw, status):
+    assert attention(**kw) == status
+    if status != P.FP8_OK:
+        assert P.lib.fp8_last_error().decode() != ""

@@ -429,7 +429,7 @@ def vendor_attention(w: Workload):
         us = float(np.median([s_.elapsed_time(e_) for s_, e_ in ev])) * 1e3
         return {"library": "torch.nn.functional.scaled_dot_product_attention (BF16)",
                 "bf16": {"median_us": round(us, 2), "tflops": round(w.flops / (us * 1e-6) / 1e12, 2)}}
-    except Exception as e:  # no fused attention on this build
+    except Exception as e:  # torch without a usable attention kernel here
         return {"library": "torch.nn.functional.scaled_dot_product_attention (BF16)", "error": repr(e)[:200]}
 
 

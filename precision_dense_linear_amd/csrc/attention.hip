@@ -11,8 +11,12 @@
 // over the visible keys (all, or causal: j <= i + seq_kv - seq_q).  Q, K, V
 // are E4M3 codes widened exactly to BF16 for the matrix cores, so both
 // products are exact and accumulate in FP32.  The softmax runs online over
-// 64-key blocks in FP32 (base-2 exponentials of the max-subtracted scores);
-// each unnormalised probability is rounded to BF16 for the second product
+// 64-key blocks in FP32: base-2 exponentials of the scaled score minus an
+// offset (one FMA each), where the offset is the running max as of the last
+// rescale -- accumulator and row sum are rescaled only when some query's
+// max has grown by more than ATT_TAU since, so the unnormalised
+// probabilities stay below 2^ATT_TAU and most blocks skip the rescale.
+// Each unnormalised probability is rounded to BF16 for the second product
 // and the row sum adds the same rounded values; the output is divided by it
 // at the end.
 //
@@ -43,6 +47,7 @@ constexpr int ATT_BM = 128;   // queries per workgroup
 constexpr int ATT_BN = 64;    // keys per step
 constexpr int ATT_NBUF = 3;   // K/V stage buffers
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float ATT_TAU = 8.0f;   // largest growth of a running max (log2 units) left unrescaled
 
 struct AttnArgs {
     const uint8_t* Q;
@@ -188,13 +193,29 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
                 v_rd[kb][m][ni] = TILE + kr * D + swz_b<D>(kr, col >> 4) * 16 + (col & 15);
             }
 
-    const float c2 = (p.scale_q[0] * p.scale_k[0]) * (p.softmax_scale * LOG2E);   // score -> log2 units
+    // score -> log2 units, kept positive so that a masked raw score of -inf
+    // stays -inf: a negative product of scales is moved onto Q (an exact
+    // sign flip of its codes), and one that underflowed to 0 becomes the
+    // least normal float (every |score| is then below 2^-100, so each
+    // exponential still rounds to 1)
+    float c2 = (p.scale_q[0] * p.scale_k[0]) * (p.softmax_scale * LOG2E);
+    if (c2 == 0.0f) c2 = 1.17549435e-38f;
+    if (c2 < 0.0f) {
+        c2 = -c2;
+        if constexpr (FASTQK) {
+#pragma unroll
+            for (int m = 0; m < D / 64; ++m) q8[m] ^= (int)0x80808080;
+        } else {
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) qf[t] = __builtin_bit_cast(v8bf, __builtin_bit_cast(v4i, qf[t]) ^ (int)0x80008000);
+        }
+    }
     v16f acc[1][DC];
 #pragma unroll
     for (int ni = 0; ni < DC; ++ni)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[0][ni][r] = 0.0f;
-    float m_run = -__builtin_inff();
+    float m_off = -__builtin_inff();   // exponent offset (log2 units; -inf: no visible key yet)
     float l_run = 0.0f;   // this lane's share of the row sum (its 32 of every 64 keys)
 
 #pragma unroll
@@ -232,34 +253,50 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
                 }
             }
         }
-        // scores in log2 units; keys past seq_kv (zero-filled) and, causal,
-        // past the query's last visible key are masked
+        // Keys past seq_kv (zero-filled) and, causal, past the query's last
+        // visible key get the raw score -inf (c2 > 0 keeps it -inf in the
+        // exponent); only edge blocks evaluate the mask.
         const int64_t key0 = (int64_t)kb * ATT_BN;
-        const bool edge = key0 + ATT_BN > Skv || (CAUSAL && key0 + ATT_BN - 1 > q0 + offs);
+        if (key0 + ATT_BN > Skv || (CAUSAL && key0 + ATT_BN - 1 > q0 + offs)) {
+            // keys 0 .. lim-1 of the block are visible to this lane's query;
+            // element r of half hb holds key 32 hb + 8 (r/4) + 4 h + r%4
+            int64_t l = Skv - key0;
+            if constexpr (CAUSAL) l = min<int64_t>(l, my_q + offs + 1 - key0);
+            const int lim = (int)max<int64_t>(0, min<int64_t>(ATT_BN, l)) - 4 * h;
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (hb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[hb][r] = -__builtin_inff();
+        }
+        // block max of the raw scores (c2 > 0: the max of the scaled ones)
         float mx = -__builtin_inff();
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float v = s[hb][r] * c2;
-                if (edge) {
-                    const int64_t key = key0 + hb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool vis = key < Skv && (!CAUSAL || key <= my_q + offs);
-                    v = vis ? v : -__builtin_inff();
-                }
-                s[hb][r] = v;
-                mx = fmaxf(mx, v);
-            }
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;   // no visible key yet
-        // (v_exp_f32 itself: results below 2^-126, far under any weight
-        // that matters, flush to zero)
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        const bool rescale = __ballot(m_new != m_run) != 0;   // (alpha is exactly 1 where the max stayed)
-        m_run = m_new;
-        // probabilities, rounded to BF16 for the second product; the row sum
-        // adds the same rounded values
+        const float mxs = mx == -__builtin_inff() ? mx : mx * c2;   // log2 units
+        // Rescale only when some query's max grew by more than ATT_TAU
+        // (wave-uniform): otherwise the exponents keep the old offset and
+        // the unnormalised probabilities stay below 2^ATT_TAU.
+        if (__ballot(mxs > m_off + ATT_TAU) != 0) {
+            const float m_new = fmaxf(m_off, mxs);
+            // (v_exp_f32 itself: results below 2^-126, far under any weight
+            // that matters, flush to zero)
+            const float alpha = m_off == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_off - m_new);
+            m_off = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int ni = 0; ni < DC; ++ni)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[0][ni][r] *= alpha;
+        }
+        // probabilities exp2(c2 s - m_off), rounded to BF16 in pairs for the
+        // second product; the row sum adds the same rounded values
+        // (v_dot2c_f32_bf16 against ones)
+        const float nb = m_off == -__builtin_inff() ? 0.0f : -m_off;
+        const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
         v8bf pf[2][2];
         float lsum = 0.0f;
 #pragma unroll
@@ -267,17 +304,15 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const __bf16 b = (__bf16)__builtin_amdgcn_exp2f(s[hb][8 * mm + e] - m_use);
-                    pf[hb][mm][e] = b;
-                    lsum += (float)b;
+                for (int e = 0; e < 8; e += 2) {
+                    const int r = 8 * mm + e;
+                    const v2bf pr = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s[hb][r], c2, nb)),
+                                     (__bf16)__builtin_amdgcn_exp2f(fmaf(s[hb][r + 1], c2, nb))};
+                    pf[hb][mm][e] = pr[0];
+                    pf[hb][mm][e + 1] = pr[1];
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
                 }
-        l_run = l_run * alpha + lsum;
-        if (rescale)   // some query's running max moved (wave-uniform)
-#pragma unroll
-            for (int ni = 0; ni < DC; ++ni)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[0][ni][r] *= alpha;
+        l_run += lsum;
         // O^T += V^T P^T over the block's four 16-key groups
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)

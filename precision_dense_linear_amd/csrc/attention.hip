@@ -222,14 +222,18 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
     for (int kb = 0; kb < ATT_NBUF - 1; ++kb)
         if (kb < nkb) issue(kb);
 
-    for (int kb = 0; kb < nkb; ++kb) {
+    // One key block; its stage buffer BUF = kb % ATT_NBUF is a compile-time
+    // constant, so every LDS read address is a per-lane register plus an
+    // immediate offset.
+    auto step = [&](const int kb, auto buf_c) {
+        constexpr int BUF = decltype(buf_c)::value;
         // the loads of block kb have landed (block kb+1's may still fly),
         // and every wave is done with the buffer block kb+2 refills
         if (kb + 1 < nkb) wait_vmcnt_lds<2 * LOADS>();
         else wait_vmcnt_lds<0>();
         __syncthreads();
         if (kb + ATT_NBUF - 1 < nkb) issue(kb + ATT_NBUF - 1);
-        const lds_u8* st = (const lds_u8*)smem + (kb % ATT_NBUF) * STAGE;
+        const lds_u8* st = (const lds_u8*)smem + BUF * STAGE;
 
         // S^T for the block's two 32-key halves
         v16f s[2];
@@ -269,12 +273,14 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
                 for (int r = 0; r < 16; ++r)
                     if (hb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[hb][r] = -__builtin_inff();
         }
-        // block max of the raw scores (c2 > 0: the max of the scaled ones)
-        float mx = -__builtin_inff();
+        // block max of the raw scores (c2 > 0: the max of the scaled ones),
+        // as four independent chains
+        float m4[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hb][r]);
+            for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[hb][r]);
+        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mxs = mx == -__builtin_inff() ? mx : mx * c2;   // log2 units
         // Rescale only when some query's max grew by more than ATT_TAU
@@ -298,7 +304,7 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
         const float nb = m_off == -__builtin_inff() ? 0.0f : -m_off;
         const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
         v8bf pf[2][2];
-        float lsum = 0.0f;
+        float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four independent partial sums
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -310,9 +316,9 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
                                      (__bf16)__builtin_amdgcn_exp2f(fmaf(s[hb][r + 1], c2, nb))};
                     pf[hb][mm][e] = pr[0];
                     pf[hb][mm][e + 1] = pr[1];
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+                    ls[e / 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls[e / 2], false);
                 }
-        l_run += lsum;
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
         // O^T += V^T P^T over the block's four 16-key groups
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
@@ -323,6 +329,12 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
                     const v2i vr = lds_read_tr8(st + v_rd[hb][mm][ni]);
                     acc[0][ni] = mfma_32x32x16_bf16(e4m3x8_to_bf16(vr[0], vr[1]), pf[hb][mm], acc[0][ni]);
                 }
+    };
+    static_assert(ATT_NBUF == 3, "the key-block loop is unrolled over the stage buffers");
+    for (int kb = 0; kb < nkb; kb += ATT_NBUF) {
+        step(kb, std::integral_constant<int, 0>{});
+        if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{});
+        if (kb + 2 < nkb) step(kb + 2, std::integral_constant<int, 2>{});
     }
     wait_vmcnt<0>();
 

@@ -28,8 +28,9 @@ __global__ void fill_f32(float* p, int n, float v) {
 
 // Block-level max of non-negative values, then one atomicMax on the float's
 // bit pattern (order-preserving for non-negative floats).
+template <int NT = kThreads>
 __device__ __forceinline__ void block_max_to(float m, float* dst) {
-    __shared__ float red[kThreads / 64];
+    __shared__ float red[NT / 64];
     m = wave_max(m);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) red[wave] = m;
@@ -37,7 +38,7 @@ __device__ __forceinline__ void block_max_to(float m, float* dst) {
     if (threadIdx.x == 0) {
         float r = red[0];
 #pragma unroll
-        for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+        for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, red[w]);
         atomicMax(reinterpret_cast<unsigned int*>(dst), __float_as_uint(r));
     }
 }
@@ -50,7 +51,12 @@ __device__ __forceinline__ void block_max_to(float m, float* dst) {
 constexpr int PT_U = 8;
 constexpr int64_t CHUNK4 = 64 * PT_U;
 
-__global__ void __launch_bounds__(kThreads) amax_kernel(const float* __restrict__ x, int64_t n, int64_t cpb,
+// amax runs 16-wave workgroups over 4x the chunks of a quantize workgroup:
+// the same waves in flight, a quarter of the atomics on the one amax word
+// (2048 of them, all landing within a few microseconds on a 64 MB tensor,
+// serialise to ~13 us).
+constexpr int kAmaxThreads = 1024;
+__global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const float* __restrict__ x, int64_t n, int64_t cpb,
                                                         float* amax) {
     const int64_t n4 = n >> 2;
     const v4f* x4 = reinterpret_cast<const v4f*>(x);
@@ -58,7 +64,7 @@ __global__ void __launch_bounds__(kThreads) amax_kernel(const float* __restrict_
     const int64_t c0 = (int64_t)blockIdx.x * cpb;
     const int64_t c1 = min(c0 + cpb, (n4 + CHUNK4 - 1) / CHUNK4);
     float m = 0.0f;
-    for (int64_t c = c0 + wave; c < c1; c += kThreads / 64) {
+    for (int64_t c = c0 + wave; c < c1; c += kAmaxThreads / 64) {
         v4f v[PT_U];
 #pragma unroll
         for (int u = 0; u < PT_U; ++u) {
@@ -71,7 +77,7 @@ __global__ void __launch_bounds__(kThreads) amax_kernel(const float* __restrict_
     }
     if (blockIdx.x == 0)
         for (int64_t j = (n4 << 2) + threadIdx.x; j < n; j += blockDim.x) m = fmaxf(m, fabsf(x[j]));
-    block_max_to(m, amax);
+    block_max_to<kAmaxThreads>(m, amax);
 }
 
 // Codes for n floats with the scale derived from *amax: the chunk partition
@@ -341,7 +347,8 @@ hipError_t launch_quantize_2of4(const float* w, int64_t K, int64_t N, uint8_t* v
     const int64_t nchunks = ((n >> 2) + CHUNK4 - 1) / CHUNK4;
     const int64_t cpb = nchunks < 2048 ? 1 : (nchunks + 2047) / 2048;
     const int64_t blocks = nchunks < 1 ? 1 : (nchunks + cpb - 1) / cpb;
-    if (n > 0) hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, w, n, cpb, amax);
+    const int64_t acpb = cpb * (kAmaxThreads / kThreads), ablocks = nchunks < 1 ? 1 : (nchunks + acpb - 1) / acpb;
+    if (n > 0) hipLaunchKernelGGL(amax_kernel, dim3((unsigned)ablocks), dim3(kAmaxThreads), 0, s, w, n, acpb, amax);
     const int64_t waves = (K / 32) * ((N + 63) / 64);
     const int64_t qblocks = waves < 1 ? 1 : (waves + kThreads / 64 - 1) / (kThreads / 64);
     hipLaunchKernelGGL(quantize_2of4_kernel, dim3((unsigned)qblocks), dim3(kThreads), 0, s, w, K, N,
@@ -356,8 +363,9 @@ hipError_t launch_quantize_pertensor(const float* x, int64_t n, uint8_t* q, floa
     const int64_t nchunks = ((n >> 2) + CHUNK4 - 1) / CHUNK4;
     const int64_t cpb = nchunks < 2048 ? 1 : (nchunks + 2047) / 2048;
     const int64_t blocks = nchunks < 1 ? 1 : (nchunks + cpb - 1) / cpb;
+    const int64_t acpb = cpb * (kAmaxThreads / kThreads), ablocks = nchunks < 1 ? 1 : (nchunks + acpb - 1) / acpb;
     if (n > 0)
-        hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, n, cpb, amax);
+        hipLaunchKernelGGL(amax_kernel, dim3((unsigned)ablocks), dim3(kAmaxThreads), 0, s, x, n, acpb, amax);
     if (fmt == 0)
         hipLaunchKernelGGL(quantize_kernel<0>, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, n, cpb,
                            (const float*)amax, q, scale);

@@ -47,10 +47,10 @@ def attention(qq, qk, qv, scale_q, scale_k, scale_v, softmax_scale, causal=False
     """qq [BH, Sq, D], qk and qv [BH, Skv, D] E4M3 codes (uint8); returns
     float64 arrays:
       O      [BH, Sq, D]  the attention output;
-      wabs   [BH, Sq, D]  scale_v * sum_j P[i, j] * |V[h, j, d]| (the scale of
+      wabs   [BH, Sq, D]  |scale_v| * sum_j P[i, j] * |V[h, j, d]| (the scale of
                           the second product's rounding errors);
-      sabs   [BH, Sq]     max over visible j of (scale_q * scale_k *
-                          softmax_scale) * sum_d |Q[h, i, d] * K[h, j, d]|
+      sabs   [BH, Sq]     max over visible j of |scale_q * scale_k *
+                          softmax_scale| * sum_d |Q[h, i, d] * K[h, j, d]|
                           (the scale of the first product's);
       smax   [BH, Sq]     max over visible j of |S[i, j]|."""
     Q, K, V = _decode(qq), _decode(qk), _decode(qv)
@@ -72,8 +72,8 @@ def attention(qq, qk, qv, scale_q, scale_k, scale_v, softmax_scale, causal=False
         L = E.sum(axis=1)
         W = np.divide(E, L[:, None], out=np.zeros_like(E), where=L[:, None] > 0)
         O[h] = (W @ V[h]) * float(scale_v)
-        wabs[h] = (W @ np.abs(V[h])) * float(scale_v)
-        A = np.where(vis, (np.abs(Q[h]) @ np.abs(K[h]).T) * c, 0.0)
+        wabs[h] = (W @ np.abs(V[h])) * abs(float(scale_v))
+        A = np.where(vis, (np.abs(Q[h]) @ np.abs(K[h]).T) * abs(c), 0.0)
         sabs[h] = A.max(axis=1, initial=0.0)
         smax[h] = np.where(vis, np.abs(S), 0.0).max(axis=1, initial=0.0)
     return O, wabs, sabs, smax

@@ -14,7 +14,8 @@ from the oracle; with Q K^T on the FP8 matrix cores (fast=True) dS grows by
 products.  Shapes: ragged query and key counts on both head
 dimensions, causal and not, all output types; the LLM shape (32 heads,
 sequence 4096, head dimension 128) on every output; decode (one query);
-queries without visible keys; no keys at all; equal scores (the mean of V)."""
+queries without visible keys; no keys at all; equal scores (the mean of V);
+negative scales and a scale product that underflows binary32."""
 import numpy as np
 import pytest
 import torch
@@ -120,6 +121,26 @@ def test_queries_without_keys_and_no_keys():
     O = torch.full((2, 50, 64), float("nan"), device=DEV)
     P.fp8_attention(q, empty, empty, sq, sq, sq, 0.125, False, torch.float32, O=O)
     assert torch.count_nonzero(O).item() == 0
+
+
+@pytest.mark.parametrize("fast", [False, True])
+def test_negative_and_underflowing_scale_products(fast):
+    q, sq, oq, osq = quantized((2, 150, 128), 51)
+    k, sk, ok, osk = quantized((2, 200, 128), 52)
+    v, sv, ov, osv = quantized((2, 200, 128), 53)
+    ss = float(np.float32(1 / np.sqrt(128)))
+    tiny = np.float32(1e-30)
+    dtiny = torch.full((1,), float(tiny), device=DEV)
+    for causal in (False, True):
+        # a negative scale product (the kernel moves the sign onto Q's codes)
+        O = P.fp8_attention(q, k, v, -sq, sk, -sv, ss, causal, torch.bfloat16, fast=fast)
+        Oex, wabs, sabs, smax = OA.attention(oq, ok, ov, -osq, osk, -osv, ss, causal)
+        check(O, Oex, wabs, sabs, smax, 200, 128, "negative scales causal=%s fast=%s" % (causal, fast), fast=fast)
+        # scale_q * scale_k underflows to 0 in binary32: every visible score
+        # is (all but) zero, so each query averages the V rows it sees
+        O = P.fp8_attention(q, k, v, dtiny, dtiny, sv, ss, causal, torch.float32, fast=fast)
+        Oex, wabs, sabs, smax = OA.attention(oq, ok, ov, tiny, tiny, osv, ss, causal)
+        check(O, Oex, wabs, sabs, smax, 200, 128, "underflowing scales causal=%s fast=%s" % (causal, fast), fast=fast)
 
 
 def test_equal_scores_give_the_mean_of_v():

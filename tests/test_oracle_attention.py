@@ -117,6 +117,19 @@ def test_key_permutation_and_scale_invariances():
     assert np.allclose(O3, O * 0.5, rtol=1e-14, atol=1e-14 * float(np.abs(O).max()))
 
 
+def test_negative_scale_equals_negated_q_codes():
+    # S = c * (Q K^T): a negative scale_q is the same as Q with every sign bit
+    # flipped (E4M3 sign-magnitude codes) and the positive scale; the error
+    # scales stay non-negative
+    BH, Sq, Skv, D = 2, 9, 30, 64
+    qq, qk, qv = codes((BH, Sq, D), 17), codes((BH, Skv, D), 18), codes((BH, Skv, D), 19)
+    for causal in (False, True):
+        On, wn, an, mn = OA.attention(qq, qk, qv, -0.03, 0.02, -0.5, 0.125, causal)
+        Op, wp, ap, mp = OA.attention(qq ^ np.uint8(0x80), qk, qv, 0.03, 0.02, 0.5, 0.125, causal)
+        assert np.array_equal(On, -Op) and np.array_equal(wn, wp) and np.array_equal(an, ap) and np.array_equal(mn, mp)
+        assert np.all(wn >= 0) and np.all(an >= 0)
+
+
 def test_flops_counts_visible_pairs():
     assert OA.flops(2, 4, 4, 8, False) == 4.0 * 2 * 16 * 8
     assert OA.flops(2, 4, 4, 8, True) == 4.0 * 2 * 10 * 8

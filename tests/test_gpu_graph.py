@@ -1,7 +1,8 @@
 """Graph capture of the hot path, through the C ABI.
 
-The per-tensor step (quantize A, quantize B, FP8 GEMM), the block-scaled step
-and the grouped (MoE) step are captured in a HIP graph (torch.cuda.CUDAGraph)
+The per-tensor step (quantize A, quantize B, FP8 GEMM), the block-scaled step,
+the grouped (MoE) step and the attention step (quantize Q, K, V, attention)
+are captured in a HIP graph (torch.cuda.CUDAGraph)
 and the graph is replayed several times, with eager work between the replays
 (new input values, stale values planted in every output and accumulator).
 Every replay must equal, bit for bit, the same calls run eagerly on the same
@@ -133,3 +134,34 @@ def test_graph_grouped_step():
         P.fp8_grouped_gemm(st["qx"], st["qw"].view(E, K, N), offs, st["sx"], st["sw"], torch.bfloat16, C=st["C"])
 
     replay_against_eager((X, Wt), make_state, step, ["qx", "qw", "sx", "sw", "ax", "aw", "C"], perturb_pair)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("fast", [False, True])
+def test_graph_attention_step(causal, fast):
+    BH, Sq, Skv, D = 4, 300, 333, 128
+    print("graph attention BH=%d Sq=%d Skv=%d D=%d causal=%s fast=%s" % (BH, Sq, Skv, D, causal, fast), flush=True)
+    rng = np.random.default_rng(29)
+    Q, K, V = (gpu(rng.standard_normal(s).astype(np.float32)) for s in ((BH, Sq, D), (BH, Skv, D), (BH, Skv, D)))
+
+    def make_state():
+        st = {"q" + n: empty_like_codes(x) for n, x in (("q", Q), ("k", K), ("v", V))}
+        for n in ("sq", "aq", "sk", "ak", "sv", "av"):
+            st[n] = torch.empty(1, device=DEV)
+        st["O"] = torch.empty((BH, Sq, D), dtype=torch.bfloat16, device=DEV)
+        return st
+
+    def step(st):
+        P.fp8_quantize(Q, st["qq"], st["sq"], st["aq"])
+        P.fp8_quantize(K, st["qk"], st["sk"], st["ak"])
+        P.fp8_quantize(V, st["qv"], st["sv"], st["av"])
+        P.fp8_attention(st["qq"], st["qk"], st["qv"], st["sq"], st["sk"], st["sv"], causal=causal, fast=fast,
+                        O=st["O"])
+
+    def perturb(inputs, i):
+        q, k, v = inputs
+        q.mul_((-1.5, 0.25, 3.0)[i % 3])
+        k.add_((0.125, -0.5, 0.0)[i % 3])
+        v.mul_((2.0, -1.0, 0.5)[i % 3])
+
+    replay_against_eager((Q, K, V), make_state, step, ["qq", "qk", "qv", "sq", "sk", "sv", "O"], perturb)

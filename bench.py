@@ -607,7 +607,9 @@ def main():
                     "gemm_pct_fp8_peak_at_sclk": round(100 * gemm_tflops / (CUS * FP8_FLOP_PER_CU_CLK * ghz / 1e3), 2)}
 
     out = {
-        "metric": "FP8 GEMM TFLOPS at M=N=K=8192 (BF16 out) + % of MI355X dense FP8 peak",
+        "metric": ("FP8 GEMM TFLOPS at M=N=K=8192 (BF16 out) + % of MI355X dense FP8 peak" if args.workload == "gemm8192"
+                   else "%s TFLOPS, %s workload (kernel alone) + %% of MI355X dense FP8 peak"
+                   % ("FP8 attention" if w.kind == "attn" else "FP8 GEMM", args.workload)),
         "value": round(gemm_tflops, 2),
         "unit": "TFLOP/s",
         "pct_fp8_peak": round(100 * gemm_tflops / FP8_PEAK_TFLOPS, 2),
@@ -622,8 +624,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.desc, "M": w.M, "N": w.N, "K": w.K,
                    "out": {torch.bfloat16: "bf16", torch.float16: "f16"}.get(w.out, "f32"),
-                   "step": "quantize A and B + GEMM",
-                   "value": "GEMM kernel alone (average launch inside the timed steps)"},
+                   "step": "quantize Q, K, V + attention" if w.kind == "attn" else "quantize A and B + GEMM",
+                   "value": "%s kernel alone (average launch inside the timed steps)"
+                            % ("attention" if w.kind == "attn" else "GEMM")},
         "step_tflops": round(w.flops / (ms_step * 1e-3) / 1e12, 2),
         "gemm_tflops": round(gemm_tflops, 2),
         "quantize_ms": round(q_ms, 4),

@@ -29,6 +29,7 @@ torch.float32, torch.bfloat16 or torch.float16.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -129,6 +130,15 @@ def _fmt_flag(t: torch.Tensor, fmt, flag: int) -> int:
     return flag if fmt == "e5m2" else 0
 
 
+_SAME_DEVICE = contextlib.nullcontext()
+
+
+def _on(dev: torch.device):
+    """The device guard for a call on dev: none when dev is already current
+    (entering torch.cuda.device costs a few microseconds per call)."""
+    return _SAME_DEVICE if dev.index == torch.cuda.current_device() else torch.cuda.device(dev)
+
+
 def _stream(dev: torch.device, stream):
     if stream is None:
         stream = torch.cuda.current_stream(dev)
@@ -156,7 +166,7 @@ def _quantize(func: str, x: torch.Tensor, q, scale, amax, stream):
     q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else q
     scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
     amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else amax
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(func, getattr(lib, func)(_ptr(x), x.numel(), _ptr(q), _ptr(scale), _ptr(amax), _stream(dev, stream)))
     return q, scale, amax
 
@@ -179,7 +189,7 @@ def _quantize_blocked(func: str, T: int, x, q, tile_scales, stream):
     q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else q
     if tile_scales is None:
         tile_scales = torch.empty((rows // T, cols // T), dtype=torch.float32, device=dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(func, getattr(lib, func)(_ptr(x), rows, cols, _ptr(q), _ptr(tile_scales), _stream(dev, stream)))
     return q, tile_scales
 
@@ -208,7 +218,7 @@ def fp8_quantize_blocked_e8m0(x: torch.Tensor, k_major=False, q=None, tile_exps=
         pitch = lambda n: (n + 3) // 4 * 4
         shape = (cols // 32, pitch(rows // 32)) if k_major else (rows // 32, pitch(cols // 32))
         tile_exps = torch.empty(shape, dtype=torch.uint8, device=dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check("fp8_quantize_blocked_e8m0", lib.fp8_quantize_blocked_e8m0(_ptr(x), rows, cols, int(bool(k_major)),
                                                                           _ptr(q), _ptr(tile_exps),
                                                                           _stream(dev, stream)))
@@ -225,7 +235,7 @@ def _quantize_grouped(func: str, x, offsets, q, scales, amax, stream):
     q = torch.zeros(x.shape, dtype=torch.uint8, device=dev) if q is None else q
     scales = torch.empty(G, dtype=torch.float32, device=dev) if scales is None else scales
     amax = torch.empty(G, dtype=torch.float32, device=dev) if amax is None else amax
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(func, getattr(lib, func)(_ptr(x), rows, cols, _ptr(offsets), G, _ptr(q), _ptr(scales), _ptr(amax),
                                         _stream(dev, stream)))
     return q, scales, amax
@@ -270,7 +280,7 @@ def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=No
     _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
-    with torch.cuda.device(A.device):
+    with _on(A.device):
         if workspace is None:
             _check("fp8_gemm", lib.fp8_gemm(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N, K,
                                             code | flags, _stream(A.device, stream)))
@@ -296,7 +306,7 @@ def fp8_gemm_noalloc(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, s
     _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
-    with torch.cuda.device(A.device):
+    with _on(A.device):
         _check("fp8_gemm_noalloc", lib.fp8_gemm_noalloc(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N,
                                                         K, code | flags, _stream(A.device, stream)))
     return C
@@ -313,7 +323,7 @@ def fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype=torch.bfloat16, C=None, strea
     _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
-    with torch.cuda.device(A.device):
+    with _on(A.device):
         _check("fp8_gemm_blockscaled", lib.fp8_gemm_blockscaled(_ptr(A), _ptr(B), _ptr(s_a), _ptr(s_b), _ptr(C),
                                                                 M, N, K, code | (FP8_BLOCK64 if block == 64 else 0),
                                                                 _stream(A.device, stream)))
@@ -331,7 +341,7 @@ def fp8_gemm_blockscaled_e8m0(A, B, e_a, e_b, out_dtype=torch.bfloat16, C=None, 
     _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
-    with torch.cuda.device(A.device):
+    with _on(A.device):
         _check("fp8_gemm_blockscaled_e8m0", lib.fp8_gemm_blockscaled_e8m0(_ptr(A), _ptr(B), _ptr(e_a), _ptr(e_b),
                                                                           _ptr(C), M, N, K, code,
                                                                           _stream(A.device, stream)))
@@ -349,7 +359,7 @@ def fp8_quantize_2of4(w: torch.Tensor, vals=None, idx=None, scale=None, amax=Non
     idx = torch.empty((K // 32, N), dtype=torch.int32, device=dev) if idx is None else idx
     scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
     amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else amax
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check("fp8_quantize_2of4", lib.fp8_quantize_2of4(_ptr(w), K, N, _ptr(vals), _ptr(idx), _ptr(scale),
                                                           _ptr(amax), _stream(dev, stream)))
     return vals, idx, scale, amax
@@ -367,7 +377,7 @@ def fp8_gemm_sparse24(A, vals, idx, scale_a, scale_b, out_dtype=torch.bfloat16, 
         tuple(A.shape), tuple(vals.shape), tuple(idx.shape)))
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
-    with torch.cuda.device(A.device):
+    with _on(A.device):
         _check("fp8_gemm_sparse24", lib.fp8_gemm_sparse24(_ptr(A), _ptr(vals), _ptr(idx), _ptr(scale_a),
                                                           _ptr(scale_b), _ptr(C), M, N, K, code,
                                                           _stream(A.device, stream)))
@@ -384,7 +394,7 @@ def fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype=torch.bfloat16, 
     _require(K2 == K and offsets.numel() == E + 1, "shape mismatch")
     code = _out_code(out_dtype)
     C = _out_tensor(C, (T, N), code, A.device)
-    with torch.cuda.device(A.device):
+    with _on(A.device):
         _check("fp8_grouped_gemm", lib.fp8_grouped_gemm(_ptr(A), _ptr(B), _ptr(offsets), E, _ptr(scale_a),
                                                         _ptr(scale_b), _ptr(C), T, N, K, code | flags,
                                                         _stream(A.device, stream)))
@@ -406,7 +416,7 @@ def fp8_attention(Q, K, V, scale_q, scale_k, scale_v, softmax_scale=None, causal
         softmax_scale = 1.0 / float(D) ** 0.5
     code = _out_code(out_dtype)
     O = _out_tensor(O, (BH, Sq, D), code, Q.device)
-    with torch.cuda.device(Q.device):
+    with _on(Q.device):
         _check("fp8_attention", lib.fp8_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(scale_q), _ptr(scale_k), _ptr(scale_v),
                                                   _ptr(O), BH, Sq, Skv, D, float(softmax_scale), int(bool(causal)),
                                                   code | (FP8_ACC_FAST if fast else 0), _stream(Q.device, stream)))

@@ -89,6 +89,10 @@ __global__ void __launch_bounds__(64 * WM * WN * KS) gemm_kernel(GemmArgs p) {
     constexpr int TM = C::TM, TN = C::TN;
     constexpr bool WIDEN = MODE != MODE_FAST && !E8 && !SP;
     static_assert(!BLOCKED || KS == 1, "block scales need whole K blocks per wave group");
+    // The configurations the dispatch uses and the tests cover; one wave
+    // group with 32 x 32 wave tiles (e.g. 64 x 64 tiles of 2 x 2 waves) gave
+    // wrong results in a trial build and is not supported.
+    static_assert(KS > 1 || (TM >= 2 && TN >= 2), "one wave group needs wave tiles of at least 64 x 64");
     static_assert(MODE != MODE_BLOCK64 || (C::WTM % 64 == 0 && C::WTN % 64 == 0),
                   "a wave tile covers whole 64x64 scale tiles");
     constexpr int EPI = (KS > 1 ? C::RED : 0) + WM * WN * TileStore<BF16, TM, TN>::LDS_BYTES;

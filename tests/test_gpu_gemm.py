@@ -93,8 +93,9 @@ def test_integer_exact_bit_for_bit(M, N, K, kind):
     """Small-integer operands with unit scales: every partial sum is an integer
     below 2^24, so FP32 accumulation is exact in any order and the GPU must
     match the oracle bit for bit (tiles of every shape class, ragged tails;
-    300 x 5648 has enough 128 x 128 tiles to be run with that class, the
-    smaller shapes up to M = 1024 go to the 32 x 64 class)."""
+    300 x 5648 has enough 128 x 128 tiles to be run with that class; the
+    other shapes up to M = 1024 have too few of them and go to the 32 x 64
+    class (M <= 64) or the 64 x 64 class)."""
     qa, va = int_codes((M, K), M * 7 + K)
     qb, vb = int_codes((K, N), N * 13 + K)
     C = P.fp8_gemm(gpu(qa), gpu(qb), scalar(1.0), scalar(1.0), torch.float32 if kind == F32 else torch.bfloat16)

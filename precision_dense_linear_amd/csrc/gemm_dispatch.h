@@ -56,7 +56,8 @@ hipError_t launch_cfg_splitk(const GemmProblem& g, hipStream_t s, int32_t splits
 //  * M <= 1024: 128 x 128 tiles, 4 waves of 64 x 64 per K half, the K range
 //    split over two wave groups (more loads in flight per tile) -- unless a
 //    plain GEMM has so few of them that they would fill under half of the
-//    CUs: then 64 x 64 tiles, 2 waves of 64 x 32 per K half (measured,
+//    CUs: then, if there are more 64 x 64 tiles than half the CUs, those
+//    tiles, 2 waves of 64 x 32 per K half, else the 32 x 64 class (measured,
 //    kernel time, exact mode: 1024^3 11.8 -> 8.6 us with 32 x 64 tiles and
 //    10.4 -> 9.8 us (event-timed) with 64 x 64; 512 x 2048 x 4096 27.0 ->
 //    18.6 and 20.4 -> 18.9 us, FP8_ACC_FAST 18.3 -> 14.0 us; 1024 x 1024 x
@@ -64,8 +65,12 @@ hipError_t launch_cfg_splitk(const GemmProblem& g, hipStream_t s, int32_t splits
 //    64-row tile reads A and B once per 64 x 64 outputs, half of B's bytes
 //    of a 32-row one, and these shapes are bound by each CU's L2 request
 //    rate; at 128 and more 128 x 128 tiles, e.g. 1024 x 2048 x 1024, the
-//    128 x 128 class stays faster; for M <= 64 the 32 x 64 class wastes
-//    fewer rows: 40 x 4096 x 4096 13.7 us against 16.6);
+//    128 x 128 class stays faster; with at most half as many 64 x 64 tiles
+//    as CUs the 32 x 64 class's twice as many workgroups win: 512 x 1024 x
+//    4096 (128 tiles) 14.8 against 17.3 us, 128 x 2048 x 8192 (64) 21.9
+//    against 26.8 us, while 768 x 768 x 2048 (144) takes 12.0 against 12.6;
+//    for M <= 64 the 32 x 64 class wastes fewer rows: 40 x 4096 x 4096 13.7
+//    us against 16.6);
 //  * larger M: 256 x 256 tiles, 4 waves of 128 x 128 -- MFMA bound.
 template <int FMT>
 hipError_t launch_gemm_t(const GemmProblem& g, hipStream_t s) {
@@ -80,7 +85,8 @@ hipError_t launch_gemm_t(const GemmProblem& g, hipStream_t s) {
     if (rows_per_problem <= 64 || (rows_per_problem <= 1024 && few_mid_tiles)) {
         const int sp = plain && g.ws_tiles > 0 ? choose_splits(tiles_of(g.M, g.N, 32, 64), g.K, 2, g.ws_tiles) : 1;
         if (sp > 1) return launch_cfg_splitk<FMT, 32, 64, 1, 2, 2, 4, 8>(g, s, sp);
-        if (rows_per_problem > 64) return launch_cfg<FMT, 64, 64, 1, 2, 2, 4, 8>(g, s);
+        if (rows_per_problem > 64 && tiles_of(g.M, g.N, 64, 64) * 4 > split_slots())
+            return launch_cfg<FMT, 64, 64, 1, 2, 2, 4, 8>(g, s);
         return launch_cfg<FMT, 32, 64, 1, 2, 2, 4, 8>(g, s);
     }
     if (rows_per_problem <= 1024) return launch_cfg<FMT, 128, 128, 2, 2, 2, 4, 8>(g, s);

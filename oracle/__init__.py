@@ -261,7 +261,10 @@ def gemm_rows(qa, qb, sa, sb, kind, rows=None):
 
     Returns (bits, exact, sumabs): bits are the once-rounded outputs (uint32
     FP32 bits or uint16 BF16 bits), exact is sa*sb*sum_k a*b in FP64 and
-    sumabs is sum_k |a*b| (unscaled)."""
+    sumabs is sum_k |a*b| (unscaled).  kind: F32 or BF16 (FP16 output:
+    gemm_rows_fmt)."""
+    if kind not in (F32, BF16):
+        raise ValueError("gemm_rows rounds to FP32 or BF16 only (kind %r); use gemm_rows_fmt for FP16" % (kind,))
     qa = _c(qa, np.uint8)
     qb = _c(qb, np.uint8)
     M, K = qa.shape

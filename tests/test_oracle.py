@@ -438,3 +438,10 @@ def test_grouped_reduces_to_per_expert_gemms_and_handles_empty_expert():
     b1, _, _ = oracle.grouped_gemm_rows(qx, qw[:1], [0, T], sx[:1], sw[:1], oracle.F32)
     b2, _, _ = oracle.gemm_rows(qx, qw[0], sx[0], sw[0], oracle.F32)
     assert np.array_equal(b1, b2)
+
+
+def test_gemm_rows_rejects_fp16_output():
+    # gemm_rows rounds to FP32 or BF16; FP16 output goes through gemm_rows_fmt
+    q = np.zeros((2, 16), np.uint8)
+    with pytest.raises(ValueError):
+        oracle.gemm_rows(q, q.T.copy(), 1.0, 1.0, oracle.F16)

@@ -300,7 +300,9 @@ def gemm_sampled(qa, qb, sa, sb, kind, ii, jj):
 def gemm_blockscaled_rows(qa, qb, s_a, s_b, kind, rows=None):
     """Block-scaled GEMM (32x32 tile scales) on the selected rows of A.
 
-    Returns (bits, fp64 sum, scaled sumabs)."""
+    Returns (bits, fp64 sum, scaled sumabs).  kind: F32 or BF16."""
+    if kind not in (F32, BF16):
+        raise ValueError("gemm_blockscaled_rows rounds to FP32 or BF16 only (kind %r)" % (kind,))
     qa = _c(qa, np.uint8)
     qb = _c(qb, np.uint8)
     s_a = _c(s_a, np.float32)

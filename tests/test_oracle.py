@@ -445,3 +445,10 @@ def test_gemm_rows_rejects_fp16_output():
     q = np.zeros((2, 16), np.uint8)
     with pytest.raises(ValueError):
         oracle.gemm_rows(q, q.T.copy(), 1.0, 1.0, oracle.F16)
+
+
+def test_gemm_blockscaled_rows_rejects_fp16_output():
+    q = np.zeros((32, 32), np.uint8)
+    sc = np.ones((1, 1), np.float32)
+    with pytest.raises(ValueError):
+        oracle.gemm_blockscaled_rows(q, q, sc, sc, oracle.F16)

@@ -11,7 +11,9 @@ path the shape lands on.  Also: the same call twice gives the same bits
 (determinism), and no output outside C is touched (a guard row after C).
 The grouped (MoE) form likewise: random expert counts (empty experts
 included, rows per expert across the class edges), random K and N, unit
-per-expert scales."""
+per-expert scales; and the block-scaled (power-of-two FP32 tile scales,
+32 or 64 tiles), E8M0 and 2:4-sparse GEMMs on random shapes of their
+granularity."""
 import numpy as np
 import pytest
 import torch
@@ -103,4 +105,77 @@ def test_random_grouped_bit_for_bit(case):
     bits, exact, _ = oracle.grouped_gemm_rows(qx, qw, off, np.ones(E, np.float32), np.ones(E, np.float32), kind,
                                               rows=np.arange(T))
     assert np.abs(exact).max(initial=0.0) < 2 ** 24
+    assert np.array_equal(got, bits), "%d of %d outputs differ" % (int((got != bits).sum()), got.size)
+
+
+def pot_scales(shape, rng, lo=0, hi=3):
+    """Power-of-two tile scales 2^e, e in [lo, hi]: with small-integer codes
+    every scaled partial sum stays an integer below 2^24 (exact in FP32)."""
+    return np.ldexp(1.0, rng.integers(lo, hi + 1, shape)).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_blockscaled_bit_for_bit(case):
+    rng = np.random.default_rng(7000 + case)
+    T = (32, 64)[int(rng.integers(0, 2))]
+    M, N, K = (T * int(rng.integers(1, n)) for n in (40 if T == 32 else 20, 40 if T == 32 else 20,
+                                                     32 if T == 32 else 16))
+    kind = (oracle.F32, oracle.BF16, oracle.F16)[int(rng.integers(0, 3))]
+    print("block-scaled case %d: T=%d %dx%dx%d kind %d" % (case, T, M, N, K, kind), flush=True)
+    qa, qb = int_codes((M, K), rng, E4M3), int_codes((K, N), rng, E4M3)
+    sa, sb = pot_scales((M // T, K // T), rng), pot_scales((K // T, N // T), rng)
+    C = P.fp8_gemm_blockscaled(torch.from_numpy(qa).to(DEV), torch.from_numpy(qb).to(DEV),
+                               torch.from_numpy(sa).to(DEV), torch.from_numpy(sb).to(DEV), OUT[kind], block=T)
+    bits, exact, _ = oracle.gemm_blockscaled_rows_t(qa, qb, sa, sb, T, kind)
+    assert np.abs(exact).max(initial=0.0) < 2 ** 24
+    got = to_bits(C)
+    assert np.array_equal(got, bits), "%d of %d outputs differ" % (int((got != bits).sum()), got.size)
+
+
+def k_major_exps(e):
+    """[tiles_mn, K/32] exponent bytes -> the library's [K/32, pitch(tiles_mn)] layout (padding 127)."""
+    t, kb = e.shape
+    out = np.full((kb, (t + 3) // 4 * 4), 127, np.uint8)
+    out[:, :t] = e.T
+    return out
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_e8m0_bit_for_bit(case):
+    rng = np.random.default_rng(8000 + case)
+    M, N, K = (32 * int(rng.integers(1, n)) for n in (40, 40, 32))
+    kind = (oracle.F32, oracle.BF16, oracle.F16)[int(rng.integers(0, 3))]
+    print("E8M0 case %d: %dx%dx%d kind %d" % (case, M, N, K, kind), flush=True)
+    qa, qb = int_codes((M, K), rng, E4M3), int_codes((K, N), rng, E4M3)
+    ea = rng.integers(127, 130, (M // 32, K // 32)).astype(np.uint8)     # 2^0 .. 2^2
+    eb = rng.integers(127, 130, (K // 32, N // 32)).astype(np.uint8)
+    C = P.fp8_gemm_blockscaled_e8m0(torch.from_numpy(qa).to(DEV), torch.from_numpy(qb).to(DEV),
+                                    torch.from_numpy(k_major_exps(ea)).to(DEV),
+                                    torch.from_numpy(k_major_exps(eb.T.copy())).to(DEV), OUT[kind])
+    bits, exact, _ = oracle.gemm_blockscaled_e8m0_rows(qa, qb, ea, eb, kind)
+    assert np.abs(exact).max(initial=0.0) < 2 ** 24
+    got = to_bits(C)
+    assert np.array_equal(got, bits), "%d of %d outputs differ" % (int((got != bits).sum()), got.size)
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_sparse24_bit_for_bit(case):
+    rng = np.random.default_rng(9000 + case)
+    M = int(rng.choice(EDGES)) if rng.random() < 0.5 else int(rng.integers(1, 1501))
+    N, K = 16 * int(rng.integers(1, 150)), 32 * int(rng.integers(1, 40))
+    kind = (oracle.F32, oracle.BF16)[int(rng.integers(0, 2))]
+    print("sparse case %d: %dx%dx%d kind %d" % (case, M, N, K, kind), flush=True)
+    qa, qb = int_codes((M, K), rng, E4M3), int_codes((K, N), rng, E4M3)
+    # 2:4 along K: zero two random entries of every group of 4 (code 0x00)
+    g = qb.reshape(K // 4, 4, N)
+    drop = np.argsort(rng.random((K // 4, 4, N)), axis=1)[:, :2, :]
+    np.put_along_axis(g, drop, 0, axis=1)
+    qb = g.reshape(K, N)
+    vals, idx = oracle.compress_2of4(qb)
+    one = torch.ones(1, device=DEV)
+    C = P.fp8_gemm_sparse24(torch.from_numpy(qa).to(DEV), torch.from_numpy(vals).to(DEV),
+                            torch.from_numpy(idx.view(np.int32)).to(DEV), one, one, OUT[kind])
+    bits, exact, _ = oracle.gemm_rows(qa, qb, 1.0, 1.0, kind)
+    assert np.abs(exact).max(initial=0.0) < 2 ** 24
+    got = to_bits(C)
     assert np.array_equal(got, bits), "%d of %d outputs differ" % (int((got != bits).sum()), got.size)

@@ -13,7 +13,9 @@ The grouped (MoE) form likewise: random expert counts (empty experts
 included, rows per expert across the class edges), random K and N, unit
 per-expert scales; and the block-scaled (power-of-two FP32 tile scales,
 32 or 64 tiles), E8M0 and 2:4-sparse GEMMs on random shapes of their
-granularity."""
+granularity; and attention on random head counts, sequence lengths, head
+dimensions, masks, modes and output types, within the bound its header
+states (tests/test_gpu_attention.py)."""
 import numpy as np
 import pytest
 import torch
@@ -179,3 +181,17 @@ def test_random_sparse24_bit_for_bit(case):
     assert np.abs(exact).max(initial=0.0) < 2 ** 24
     got = to_bits(C)
     assert np.array_equal(got, bits), "%d of %d outputs differ" % (int((got != bits).sum()), got.size)
+
+
+@pytest.mark.parametrize("case", range(15))
+def test_random_attention_within_bound(case):
+    from test_gpu_attention import run_case   # the header's bound, against the float64 oracle
+    rng = np.random.default_rng(11000 + case)
+    BH = int(rng.integers(1, 6))
+    Sq, Skv = int(rng.integers(1, 700)), int(rng.integers(1, 900))
+    D = (64, 128)[int(rng.integers(0, 2))]
+    causal, fast = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    out = (torch.float32, torch.bfloat16, torch.float16)[int(rng.integers(0, 3))]
+    print("attention case %d: BH=%d Sq=%d Skv=%d D=%d causal=%s fast=%s %s" % (case, BH, Sq, Skv, D, causal, fast, out),
+          flush=True)
+    run_case(BH, Sq, Skv, D, causal, out, seed=12000 + case, fast=fast)

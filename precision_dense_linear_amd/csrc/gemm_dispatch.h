@@ -71,7 +71,14 @@ hipError_t launch_cfg_splitk(const GemmProblem& g, hipStream_t s, int32_t splits
 //    against 26.8 us, while 768 x 768 x 2048 (144) takes 12.0 against 12.6;
 //    for M <= 64 the 32 x 64 class wastes fewer rows: 40 x 4096 x 4096 13.7
 //    us against 16.6);
-//  * larger M: 256 x 256 tiles, 4 waves of 128 x 128 -- MFMA bound.
+//  * larger M, and a plain GEMM with M <= 1024 whose 256 x 256 tiles fill at
+//    least 7/8 of the CUs with at most 1/8 of their rows padding: 256 x 256
+//    tiles, 4 waves of 128 x 128 -- MFMA bound (against the 128 x 128
+//    class, exact [FP8_ACC_FAST], event-timed: 1024 x 28672 x 8192 439 ->
+//    392 us [319 -> 198], 512 x 28672 x 8192 251 -> 212 [139 -> 96],
+//    768 x 28672 x 8192 360 -> 352 [212 -> 180]; slower with fewer tiles,
+//    1024 x 8192 x 8192 142 -> 169 [71 -> 82], or more padding, 384 x
+//    28672 x 8192 189 -> 196).
 template <int FMT>
 hipError_t launch_gemm_t(const GemmProblem& g, hipStream_t s) {
     const bool plain = g.experts == 0;
@@ -89,7 +96,14 @@ hipError_t launch_gemm_t(const GemmProblem& g, hipStream_t s) {
             return launch_cfg<FMT, 64, 64, 1, 2, 2, 4, 8>(g, s);
         return launch_cfg<FMT, 32, 64, 1, 2, 2, 4, 8>(g, s);
     }
-    if (rows_per_problem <= 1024) return launch_cfg<FMT, 128, 128, 2, 2, 2, 4, 8>(g, s);
+    if (rows_per_problem <= 1024) {
+        // a plain GEMM whose 256 x 256 tiles fill at least 7/8 of the CUs,
+        // with at most 1/8 of their rows padding: the 256 x 256 class
+        const int64_t cus = split_slots() / 2, padded = (g.M + 255) / 256 * 256;
+        if (plain && tiles_of(g.M, g.N, 256, 256) * 8 >= 7 * cus && 8 * (padded - g.M) <= g.M)
+            return launch_cfg<FMT, 256, 256, 2, 2, 1, 4, 8>(g, s);
+        return launch_cfg<FMT, 128, 128, 2, 2, 2, 4, 8>(g, s);
+    }
     return launch_cfg<FMT, 256, 256, 2, 2, 1, 4, 8>(g, s);
 }
 

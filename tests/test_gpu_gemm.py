@@ -87,15 +87,16 @@ def int_codes(shape, seed, lim=16):
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 16), (17, 48, 48), (64, 64, 128), (65, 272, 1040),
                                    (255, 528, 256), (300, 256, 512), (100, 8208, 272), (300, 5648, 272),
-                                   (1025, 64, 384), (1100, 528, 272)])
+                                   (480, 28688, 80), (1025, 64, 384), (1100, 528, 272)])
 @pytest.mark.parametrize("kind", [F32, BF16])
 def test_integer_exact_bit_for_bit(M, N, K, kind):
     """Small-integer operands with unit scales: every partial sum is an integer
     below 2^24, so FP32 accumulation is exact in any order and the GPU must
     match the oracle bit for bit (tiles of every shape class, ragged tails;
-    300 x 5648 has enough 128 x 128 tiles to be run with that class; the
-    other shapes up to M = 1024 have too few of them: 100 x 8208 goes to the
-    64 x 64 class, the rest to the 32 x 64 class)."""
+    300 x 5648 has enough 128 x 128 tiles to be run with that class;
+    480 x 28688 enough 256 x 256 tiles for that one; the other shapes up to
+    M = 1024 have too few of either: 100 x 8208 goes to the 64 x 64 class,
+    the rest to the 32 x 64 class)."""
     qa, va = int_codes((M, K), M * 7 + K)
     qb, vb = int_codes((K, N), N * 13 + K)
     C = P.fp8_gemm(gpu(qa), gpu(qb), scalar(1.0), scalar(1.0), torch.float32 if kind == F32 else torch.bfloat16)

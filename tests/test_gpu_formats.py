@@ -124,14 +124,14 @@ def int_codes(shape, seed, fmt, lim=8):
 
 
 SHAPES = [(17, 48, 48), (65, 272, 1040), (300, 256, 512), (100, 8208, 272), (300, 5648, 272), (1100, 528, 272),
-          (37, 1040, 4112)]
+          (480, 28688, 32), (37, 1040, 4112)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("fa,fb", PAIRS)
 @pytest.mark.parametrize("fast", [False, True])
 def test_formats_integer_exact_bit_for_bit(M, N, K, fa, fb, fast):
-    """Every tile class (32x64 with and without split-K, 64x64 at 100 x 8208, 128x128 at 300 x 5648, 256x256),
+    """Every tile class (32x64 with and without split-K, 64x64 at 100 x 8208 and 1100 x 528, 128x128 at 300 x 5648, 256x256 at 480 x 28688),
     both accumulation modes, all three output kinds."""
     qa, qb = int_codes((M, K), M + K, fa), int_codes((K, N), N + K, fb)
     A, B = gpu(qa), gpu(qb)

@@ -93,9 +93,9 @@ def test_integer_exact_bit_for_bit(M, N, K, kind):
     """Small-integer operands with unit scales: every partial sum is an integer
     below 2^24, so FP32 accumulation is exact in any order and the GPU must
     match the oracle bit for bit (tiles of every shape class, ragged tails;
-    300 x 5648 has enough 128 x 128 tiles to be run with that class;
-    480 x 28688 enough 256 x 256 tiles for that one; the other shapes up to
-    M = 1024 have too few of either: 100 x 8208 goes to the 64 x 64 class,
+    480 x 28688 has enough 256 x 256 tiles to be run with that class,
+    300 x 5648 enough 128 x 128 tiles for that one; the other shapes have
+    too few of either: 100 x 8208 and 1100 x 528 go to the 64 x 64 class,
     the rest to the 32 x 64 class)."""
     qa, va = int_codes((M, K), M * 7 + K)
     qb, vb = int_codes((K, N), N * 13 + K)

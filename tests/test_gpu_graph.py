@@ -66,10 +66,10 @@ def perturb_pair(inputs, i):
     B.add_((0.125, -0.5, 0.0)[i % 3])
 
 
-# 256x256 tiles; 128x128 tiles; 32x64 tiles with split-K; 64x64 tiles for a plain M <= 1024 GEMM; the
-# skinny class (M <= 16) with K split 8 ways
-@pytest.mark.parametrize("M,N,K", [(1100, 528, 272), (300, 5648, 272), (40, 4096, 4096), (1024, 1024, 1024),
-                                   (16, 8192, 4096)])
+# 256x256 tiles; 128x128 tiles; 32x64 tiles with split-K; 64x64 tiles (two shapes); the skinny class (M <= 16)
+# with K split 8 ways
+@pytest.mark.parametrize("M,N,K", [(480, 28688, 80), (300, 5648, 272), (40, 4096, 4096), (1024, 1024, 1024),
+                                   (1100, 528, 272), (16, 8192, 4096)])
 @pytest.mark.parametrize("fast", [False, True])
 def test_graph_pertensor_step(M, N, K, fast):
     print("graph per-tensor %dx%dx%d fast=%s" % (M, N, K, fast), flush=True)

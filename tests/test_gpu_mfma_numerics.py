@@ -152,7 +152,7 @@ def normal_codes(shape, seed):
 # 32 x 64 with K split over 8 workgroups, 64 x 64 with two wave groups,
 # 128 x 128 with two wave groups, 256 x 256 with one
 SHAPES = [(40, 256, 1040, False, "32x64"), (20, 1024, 8192, True, "32x64 split-K x8"),
-          (200, 4160, 528, False, "64x64"), (300, 5648, 528, False, "128x128"), (1100, 256, 784, False, "256x256")]
+          (200, 4160, 528, False, "64x64"), (300, 5648, 528, False, "128x128"), (2048, 7168, 528, False, "256x256")]
 
 
 @pytest.mark.parametrize("M,N,K,ws,cls", SHAPES)

@@ -5,7 +5,7 @@
 // 2^(e - 127)), so no vector-ALU promotion step is needed.  Tile loop of
 // gemm_kernel.h in MODE_E8M0; the accumulators stay in the accumulation
 // registers.
-#include "gemm_kernel.h"
+#include "gemm_dispatch.h"
 
 namespace fp8k {
 
@@ -29,10 +29,10 @@ hipError_t launch_gemm_blockscaled_e8m0(const uint8_t* A, const uint8_t* B, cons
     g.e8_a = e8_a;
     g.e8_b = e8_b;
     if (K == 0) return fill_zero(C, M * N * (out == 0 ? 4 : 2), s);  // empty sums: C = 0
-    // the shape classes of the per-tensor GEMM: 256 x 256 tiles once M is
-    // large enough to fill the GPU with them, else 128 x 128
-    if (M <= 1024) return launch_mode<128, 128, 2, 2, 1, 4, 8, MODE_E8M0>(g, s);
-    return launch_mode<256, 256, 2, 2, 1, 4, 8, MODE_E8M0>(g, s);
+    // 256 x 256 tiles when they fill the GPU (as for the per-tensor GEMM),
+    // else 128 x 128
+    if (fills_with_256(M, N)) return launch_mode<256, 256, 2, 2, 1, 4, 8, MODE_E8M0>(g, s);
+    return launch_mode<128, 128, 2, 2, 1, 4, 8, MODE_E8M0>(g, s);
 }
 
 }  // namespace fp8k

@@ -16,6 +16,14 @@ int choose_splits(int64_t tiles, int64_t K, int per_cu, int64_t capacity);
 
 inline int64_t tiles_of(int64_t M, int64_t N, int BM, int BN) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
+// Whether the 256 x 256 class takes a plain M x N GEMM: M > 64 and its
+// tiles fill at least 7/8 of the CUs with at most 1/8 of their rows padding.
+inline bool fills_with_256(int64_t M, int64_t N) {
+    const int64_t cus = split_slots() / 2;   // split_slots() is twice the CU count
+    const int64_t padded = (M + 255) / 256 * 256;
+    return M > 64 && tiles_of(M, N, 256, 256) * 8 >= 7 * cus && 8 * (padded - M) <= M;
+}
+
 // Plain GEMM with M <= 16 (gemm_skinny.hip): the split count it would use
 // (0 when the skinny class does not take the problem), and the launch.
 int skinny_splits(const GemmProblem& g);
@@ -91,10 +99,8 @@ hipError_t launch_gemm_t(const GemmProblem& g, hipStream_t s) {
         const int sk = skinny_splits(g);
         if (sk > 0) return launch_skinny<FMT>(g, s, sk);
     }
-    const int64_t cus = split_slots() / 2;   // split_slots() is twice the CU count
-    const int64_t padded = (g.M + 255) / 256 * 256;
-    if (g.M > 64 && tiles_of(g.M, g.N, 256, 256) * 8 >= 7 * cus && 8 * (padded - g.M) <= g.M)
-        return launch_cfg<FMT, 256, 256, 2, 2, 1, 4, 8>(g, s);
+    const int64_t cus = split_slots() / 2;
+    if (fills_with_256(g.M, g.N)) return launch_cfg<FMT, 256, 256, 2, 2, 1, 4, 8>(g, s);
     if (g.M > 64 && tiles_of(g.M, g.N, 128, 128) * 2 >= cus) return launch_cfg<FMT, 128, 128, 2, 2, 2, 4, 8>(g, s);
     const int sp = g.ws_tiles > 0 ? choose_splits(tiles_of(g.M, g.N, 32, 64), g.K, 2, g.ws_tiles) : 1;
     if (sp > 1) return launch_cfg_splitk<FMT, 32, 64, 1, 2, 2, 4, 8>(g, s, sp);

@@ -6,7 +6,7 @@
 // column and 32-deep K block, [K/32][N] -- and fed to
 // v_smfmac_f32_32x32x64_fp8_fp8, which multiplies 64 K per instruction at
 // twice the dense rate.  Tile loop of gemm_kernel.h in MODE_SPARSE.
-#include "gemm_kernel.h"
+#include "gemm_dispatch.h"
 
 namespace fp8k {
 
@@ -30,10 +30,10 @@ hipError_t launch_gemm_sparse24(const uint8_t* A, const uint8_t* Bv, const uint3
     g.fast_acc = 1;
     g.fmt = 0;
     g.sp_idx = Bi;
-    // the shape classes of the per-tensor GEMM: 256 x 256 tiles once M is
-    // large enough to fill the GPU with them, else 128 x 128
-    if (M <= 1024) return launch_mode<128, 128, 2, 2, 1, 4, 8, MODE_SPARSE>(g, s);
-    return launch_mode<256, 256, 2, 2, 1, 4, 8, MODE_SPARSE>(g, s);
+    // 256 x 256 tiles when they fill the GPU (as for the per-tensor GEMM),
+    // else 128 x 128
+    if (fills_with_256(M, N)) return launch_mode<256, 256, 2, 2, 1, 4, 8, MODE_SPARSE>(g, s);
+    return launch_mode<128, 128, 2, 2, 1, 4, 8, MODE_SPARSE>(g, s);
 }
 
 }  // namespace fp8k

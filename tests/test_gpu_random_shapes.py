@@ -52,7 +52,7 @@ def draw(i):
     return M, N, K, fa, fb, kind, bool(rng.integers(0, 2)), bool(rng.integers(0, 2)), rng
 
 
-@pytest.mark.parametrize("case", range(100))
+@pytest.mark.parametrize("case", range(400))
 def test_random_shape_bit_for_bit(case):
     M, N, K, fa, fb, kind, fast, ws, rng = draw(case)
     print("case %d: %dx%dx%d %s x %s kind %d fast=%s ws=%s" % (case, M, N, K, NAME[fa], NAME[fb], kind, fast, ws),
@@ -75,7 +75,7 @@ def test_random_shape_bit_for_bit(case):
     assert np.array_equal(first, bits), "%d of %d outputs differ" % (int((first != bits).sum()), first.size)
 
 
-@pytest.mark.parametrize("case", range(30))
+@pytest.mark.parametrize("case", range(120))
 def test_random_grouped_bit_for_bit(case):
     rng = np.random.default_rng(5000 + case)
     E = int(rng.integers(1, 13))
@@ -116,7 +116,7 @@ def pot_scales(shape, rng, lo=0, hi=3):
     return np.ldexp(1.0, rng.integers(lo, hi + 1, shape)).astype(np.float32)
 
 
-@pytest.mark.parametrize("case", range(20))
+@pytest.mark.parametrize("case", range(60))
 def test_random_blockscaled_bit_for_bit(case):
     rng = np.random.default_rng(7000 + case)
     T = (32, 64)[int(rng.integers(0, 2))]
@@ -142,7 +142,7 @@ def k_major_exps(e):
     return out
 
 
-@pytest.mark.parametrize("case", range(20))
+@pytest.mark.parametrize("case", range(60))
 def test_random_e8m0_bit_for_bit(case):
     rng = np.random.default_rng(8000 + case)
     M, N, K = (32 * int(rng.integers(1, n)) for n in (40, 40, 32))
@@ -160,7 +160,7 @@ def test_random_e8m0_bit_for_bit(case):
     assert np.array_equal(got, bits), "%d of %d outputs differ" % (int((got != bits).sum()), got.size)
 
 
-@pytest.mark.parametrize("case", range(20))
+@pytest.mark.parametrize("case", range(60))
 def test_random_sparse24_bit_for_bit(case):
     rng = np.random.default_rng(9000 + case)
     M = int(rng.choice(EDGES)) if rng.random() < 0.5 else int(rng.integers(1, 1501))
@@ -183,7 +183,7 @@ def test_random_sparse24_bit_for_bit(case):
     assert np.array_equal(got, bits), "%d of %d outputs differ" % (int((got != bits).sum()), got.size)
 
 
-@pytest.mark.parametrize("case", range(15))
+@pytest.mark.parametrize("case", range(40))
 def test_random_attention_within_bound(case):
     from test_gpu_attention import run_case   # the header's bound, against the float64 oracle
     rng = np.random.default_rng(11000 + case)

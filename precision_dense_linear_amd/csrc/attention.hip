@@ -13,9 +13,12 @@
 // products are exact and accumulate in FP32.  The softmax runs online over
 // 64-key blocks in FP32: base-2 exponentials of the scaled score minus an
 // offset (one FMA each), where the offset is the running max as of the last
-// rescale -- accumulator and row sum are rescaled only when some query's
-// max has grown by more than ATT_TAU since, so the unnormalised
-// probabilities stay below 2^ATT_TAU and most blocks skip the rescale.
+// rescale.  A block is first computed with the current offsets and no block
+// max; only when a lane's share of the block's row sum exceeds ATT_PMAX (or
+// overflowed) -- or a query has no offset yet -- does it take the block
+// max, move the offsets to the new maxima, rescale accumulator and row sum,
+// and compute the block again.  Most blocks thus skip both the max and the
+// rescale, and every unnormalised probability kept is at most ATT_PMAX.
 // Each unnormalised probability is rounded to BF16 for the second product
 // and the row sum adds the same rounded values; the output is divided by it
 // at the end.
@@ -47,7 +50,7 @@ constexpr int ATT_BM = 128;   // queries per workgroup
 constexpr int ATT_BN = 64;    // keys per step
 constexpr int ATT_NBUF = 3;   // K/V stage buffers
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float ATT_TAU = 8.0f;   // largest growth of a running max (log2 units) left unrescaled
+constexpr float ATT_PMAX = 65536.0f;   // bound on a lane's share of a block's row sum (so on each probability kept)
 
 struct AttnArgs {
     const uint8_t* Q;
@@ -273,20 +276,49 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
                 for (int r = 0; r < 16; ++r)
                     if (hb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[hb][r] = -__builtin_inff();
         }
-        // block max of the raw scores (c2 > 0: the max of the scaled ones),
-        // as four independent chains
-        float m4[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+        // probabilities exp2(c2 s - m_off), rounded to BF16 in pairs for the
+        // second product, and this lane's share of the row sum over the same
+        // rounded values (v_dot2c_f32_bf16 against ones)
+        const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
+        v8bf pf[2][2];
+        auto probs = [&](const float nb) {
+            float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four independent partial sums
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+            for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[hb][r]);
-        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mxs = mx == -__builtin_inff() ? mx : mx * c2;   // log2 units
-        // Rescale only when some query's max grew by more than ATT_TAU
-        // (wave-uniform): otherwise the exponents keep the old offset and
-        // the unnormalised probabilities stay below 2^ATT_TAU.
-        if (__ballot(mxs > m_off + ATT_TAU) != 0) {
+                for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const int r = 8 * mm + e;
+                        const v2bf pr = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s[hb][r], c2, nb)),
+                                         (__bf16)__builtin_amdgcn_exp2f(fmaf(s[hb][r + 1], c2, nb))};
+                        pf[hb][mm][e] = pr[0];
+                        pf[hb][mm][e + 1] = pr[1];
+                        ls[e / 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls[e / 2], false);
+                    }
+            return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        };
+        // First with the current offsets and no block max: kept when every
+        // lane's share of the sum is at most ATT_PMAX, so that no
+        // probability exceeds it (an overflow to inf fails the test too).
+        bool remax = __ballot(m_off == -__builtin_inff()) != 0;
+        float lsum = 0.0f;
+        if (!remax) {
+            lsum = probs(-m_off);
+            remax = __ballot(!(lsum <= ATT_PMAX)) != 0;
+        }
+        if (remax) {
+            // block max of the raw scores (c2 > 0: the max of the scaled
+            // ones), as four independent chains; every query's offset moves
+            // to its max so far, and the block is computed again
+            float m4[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[hb][r]);
+            float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mxs = mx == -__builtin_inff() ? mx : mx * c2;   // log2 units
             const float m_new = fmaxf(m_off, mxs);
             // (v_exp_f32 itself: results below 2^-126, far under any weight
             // that matters, flush to zero)
@@ -297,28 +329,9 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
             for (int ni = 0; ni < DC; ++ni)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[0][ni][r] *= alpha;
+            lsum = probs(m_off == -__builtin_inff() ? 0.0f : -m_off);
         }
-        // probabilities exp2(c2 s - m_off), rounded to BF16 in pairs for the
-        // second product; the row sum adds the same rounded values
-        // (v_dot2c_f32_bf16 against ones)
-        const float nb = m_off == -__builtin_inff() ? 0.0f : -m_off;
-        const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
-        v8bf pf[2][2];
-        float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four independent partial sums
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const int r = 8 * mm + e;
-                    const v2bf pr = {(__bf16)__builtin_amdgcn_exp2f(fmaf(s[hb][r], c2, nb)),
-                                     (__bf16)__builtin_amdgcn_exp2f(fmaf(s[hb][r + 1], c2, nb))};
-                    pf[hb][mm][e] = pr[0];
-                    pf[hb][mm][e + 1] = pr[1];
-                    ls[e / 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls[e / 2], false);
-                }
-        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        l_run += lsum;
         // O^T += V^T P^T over the block's four 16-key groups
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)

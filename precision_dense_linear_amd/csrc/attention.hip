@@ -237,6 +237,15 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
         __syncthreads();
         if (kb + ATT_NBUF - 1 < nkb) issue(kb + ATT_NBUF - 1);
         const lds_u8* st = (const lds_u8*)smem + BUF * STAGE;
+        // the block's V fragments, read ahead of the first product and the
+        // softmax so that the LDS latency hides behind them
+        v2i vf[2][2][DC];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int ni = 0; ni < DC; ++ni) vf[hb][mm][ni] = lds_read_tr8(st + v_rd[hb][mm][ni]);
 
         // S^T for the block's two 32-key halves
         v16f s[2];
@@ -339,7 +348,7 @@ __global__ void __launch_bounds__(256, 2) attention_kernel(AttnArgs p) {
             for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
                 for (int ni = 0; ni < DC; ++ni) {
-                    const v2i vr = lds_read_tr8(st + v_rd[hb][mm][ni]);
+                    const v2i vr = vf[hb][mm][ni];
                     acc[0][ni] = mfma_32x32x16_bf16(e4m3x8_to_bf16(vr[0], vr[1]), pf[hb][mm], acc[0][ni]);
                 }
     };

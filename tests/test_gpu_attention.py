@@ -15,7 +15,8 @@ products.  Shapes: ragged query and key counts on both head
 dimensions, causal and not, all output types; the LLM shape (32 heads,
 sequence 4096, head dimension 128) on every output; decode (one query);
 queries without visible keys; no keys at all; equal scores (the mean of V);
-negative scales and a scale product that underflows binary32."""
+negative scales and a scale product that underflows binary32; scores that
+grow along the keys (the running max moves in the middle of the key loop)."""
 import numpy as np
 import pytest
 import torch
@@ -153,3 +154,26 @@ def test_equal_scores_give_the_mean_of_v():
     mean = oracle.decode(ov).mean(axis=1) * float(osv)            # every probability is exactly 1
     assert np.allclose(O, np.broadcast_to(mean[:, None, :], O.shape), rtol=0,
                        atol=2.0 ** -20 * float(np.abs(oracle.decode(ov)).max()) * float(osv))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("ss,fast", [(0.25, False), (1.0, False), (4.0, False), (0.25, True)])
+def test_scores_growing_along_the_keys(ss, fast, causal):
+    """Key rows scaled up along the sequence (x1 to x4), so a query's running
+    max keeps growing from block to block -- by a few log2 units at the
+    smallest score scale, by far more than the largest finite exponential at
+    the largest -- and the lazily kept exponent offsets must be moved (and the
+    accumulators rescaled) in the middle of the key loop."""
+    BH, Sq, Skv, D = 2, 130, 700, 128
+    rng = np.random.default_rng(61)
+    xq = rng.standard_normal((BH, Sq, D)).astype(np.float32)
+    ramp = (1.0 + 3.0 * np.arange(Skv) / (Skv - 1)).astype(np.float32)
+    xk = (rng.standard_normal((BH, Skv, D)) * ramp[None, :, None]).astype(np.float32)
+    xv = rng.standard_normal((BH, Skv, D)).astype(np.float32)
+    (q, sq, _), (k, sk, _), (v, sv, _) = (P.fp8_quantize(gpu(x)) for x in (xq, xk, xv))
+    (oq, osq, _), (ok, osk, _), (ov, osv, _) = (oracle.quantize_pertensor(x) for x in (xq, xk, xv))
+    s32 = float(np.float32(ss))
+    O = P.fp8_attention(q, k, v, sq, sk, sv, s32, causal, torch.float32, fast=fast)
+    torch.cuda.synchronize()
+    Oex, wabs, sabs, smax = OA.attention(oq, ok, ov, osq, osk, osv, s32, causal)
+    check(O, Oex, wabs, sabs, smax, Skv, D, "growing scores ss=%g causal=%s fast=%s" % (ss, causal, fast), fast=fast)

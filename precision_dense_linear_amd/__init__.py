@@ -160,12 +160,37 @@ def _require(cond: bool, msg: str):
         raise ValueError(msg)
 
 
+_CODES = (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2)
+_F32 = (torch.float32,)
+_OUT_DTYPE = {FP8_OUT_F32: torch.float32, FP8_OUT_BF16: torch.bfloat16, FP8_OUT_F16: torch.float16}
+
+
+def _arg(t, name: str, dev, dtypes, numel=None, at_least=False):
+    """Checks a tensor before its pointer goes to the library (which can check
+    sizes but not pointers): a contiguous tensor on the operands' GPU, of one
+    of dtypes, with numel elements (at least numel with at_least)."""
+    _require(isinstance(t, torch.Tensor), "%s must be a torch tensor" % name)
+    _require(t.is_cuda, "%s must be a GPU tensor" % name)
+    _require(t.device == dev, "%s is on %s, the operands on %s" % (name, t.device, dev))
+    _require(t.dtype in dtypes, "%s must be %s, got %s" % (name, " or ".join(map(str, dtypes)), t.dtype))
+    _require(t.is_contiguous(), "%s must be contiguous" % name)
+    if numel is not None:
+        n = t.numel()
+        _require(n >= numel if at_least else n == numel, "%s has %d elements where %s%d are needed" % (
+            name, n, "at least " if at_least else "", numel))
+    return t
+
+
+def _out_arg(C, name: str, dev, code: int, numel: int):
+    return _arg(C, name, dev, (_OUT_DTYPE[code],), numel)
+
+
 def _quantize(func: str, x: torch.Tensor, q, scale, amax, stream):
     _require(x.is_cuda and x.dtype == torch.float32 and x.is_contiguous(), "x must be a contiguous float32 GPU tensor")
     dev = x.device
-    q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else q
-    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
-    amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else amax
+    q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else _arg(q, "q", dev, _CODES, x.numel())
+    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else _arg(scale, "scale", dev, _F32, 1, True)
+    amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else _arg(amax, "amax", dev, _F32, 1, True)
     with _on(dev):
         _check(func, getattr(lib, func)(_ptr(x), x.numel(), _ptr(q), _ptr(scale), _ptr(amax), _stream(dev, stream)))
     return q, scale, amax
@@ -186,9 +211,11 @@ def _quantize_blocked(func: str, T: int, x, q, tile_scales, stream):
              "x must be a contiguous 2-D float32 GPU tensor")
     rows, cols = x.shape
     dev = x.device
-    q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else q
+    q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else _arg(q, "q", dev, _CODES, x.numel())
     if tile_scales is None:
         tile_scales = torch.empty((rows // T, cols // T), dtype=torch.float32, device=dev)
+    else:
+        _arg(tile_scales, "tile_scales", dev, _F32, (rows // T) * (cols // T), True)
     with _on(dev):
         _check(func, getattr(lib, func)(_ptr(x), rows, cols, _ptr(q), _ptr(tile_scales), _stream(dev, stream)))
     return q, tile_scales
@@ -213,11 +240,13 @@ def fp8_quantize_blocked_e8m0(x: torch.Tensor, k_major=False, q=None, tile_exps=
              "x must be a contiguous 2-D float32 GPU tensor")
     rows, cols = x.shape
     dev = x.device
-    q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else q
+    q = torch.empty(x.shape, dtype=torch.uint8, device=dev) if q is None else _arg(q, "q", dev, _CODES, x.numel())
+    pitch = lambda n: (n + 3) // 4 * 4
+    shape = (cols // 32, pitch(rows // 32)) if k_major else (rows // 32, pitch(cols // 32))
     if tile_exps is None:
-        pitch = lambda n: (n + 3) // 4 * 4
-        shape = (cols // 32, pitch(rows // 32)) if k_major else (rows // 32, pitch(cols // 32))
         tile_exps = torch.empty(shape, dtype=torch.uint8, device=dev)
+    else:
+        _arg(tile_exps, "tile_exps", dev, (torch.uint8,), shape[0] * shape[1], True)
     with _on(dev):
         _check("fp8_quantize_blocked_e8m0", lib.fp8_quantize_blocked_e8m0(_ptr(x), rows, cols, int(bool(k_major)),
                                                                           _ptr(q), _ptr(tile_exps),
@@ -228,13 +257,14 @@ def fp8_quantize_blocked_e8m0(x: torch.Tensor, k_major=False, q=None, tile_exps=
 def _quantize_grouped(func: str, x, offsets, q, scales, amax, stream):
     _require(x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 2,
              "x must be a contiguous 2-D float32 GPU tensor")
-    _require(offsets.is_cuda and offsets.dtype == torch.int32, "offsets must be an int32 GPU tensor")
     rows, cols = x.shape
-    G = offsets.numel() - 1
     dev = x.device
-    q = torch.zeros(x.shape, dtype=torch.uint8, device=dev) if q is None else q
-    scales = torch.empty(G, dtype=torch.float32, device=dev) if scales is None else scales
-    amax = torch.empty(G, dtype=torch.float32, device=dev) if amax is None else amax
+    _arg(offsets, "offsets", dev, (torch.int32,))
+    G = offsets.numel() - 1
+    q = torch.zeros(x.shape, dtype=torch.uint8, device=dev) if q is None else _arg(q, "q", dev, _CODES, x.numel())
+    scales = torch.empty(G, dtype=torch.float32, device=dev) if scales is None else _arg(scales, "scales", dev, _F32,
+                                                                                          G, True)
+    amax = torch.empty(G, dtype=torch.float32, device=dev) if amax is None else _arg(amax, "amax", dev, _F32, G, True)
     with _on(dev):
         _check(func, getattr(lib, func)(_ptr(x), rows, cols, _ptr(offsets), G, _ptr(q), _ptr(scales), _ptr(amax),
                                         _stream(dev, stream)))
@@ -251,11 +281,28 @@ def fp8_quantize_grouped_e5m2(x: torch.Tensor, offsets: torch.Tensor, q=None, sc
     return _quantize_grouped("fp8_quantize_grouped_e5m2", x, offsets, q, scales, amax, stream)
 
 
-def _out_tensor(C, shape, code, dev):
+def _out_tensor(C, shape, code, dev, name="C"):
     if C is not None:
-        return C
-    dt = {FP8_OUT_F32: torch.float32, FP8_OUT_BF16: torch.bfloat16, FP8_OUT_F16: torch.float16}[code]
-    return torch.empty(shape, dtype=dt, device=dev)
+        n = 1
+        for d in shape:
+            n *= d
+        return _out_arg(C, name, dev, code, n)
+    return torch.empty(shape, dtype=_OUT_DTYPE[code], device=dev)
+
+
+def _operands(A, B, a_dims=2, b_dims=2):
+    """The two FP8 operands as contiguous GPU code tensors on one device."""
+    _require(isinstance(A, torch.Tensor) and A.is_cuda, "A must be a GPU tensor")
+    dev = A.device
+    _arg(A, "A", dev, _CODES)
+    _arg(B, "B", dev, _CODES)
+    _require(A.dim() == a_dims and B.dim() == b_dims, "A must have %d dimensions and B %d" % (a_dims, b_dims))
+    return dev
+
+
+def _scales(dev, n, **named):
+    for name, t in named.items():
+        _arg(t, name, dev, _F32, n, True)
 
 
 def gemm_workspace(device=None, nbytes: int = FP8_GEMM_WORKSPACE_BYTES) -> torch.Tensor:
@@ -274,10 +321,12 @@ def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=No
     fp8_gemm_ws, which may split K across workgroups for outputs too small to
     fill the GPU; calls sharing a workspace must be ordered (one stream)."""
     flags = _fmt_flag(A, a_fmt, FP8_A_E5M2) | _fmt_flag(B, b_fmt, FP8_B_E5M2) | (FP8_ACC_FAST if fast else 0)
+    dev = _operands(A, B)
     A, B = _codes(A), _codes(B)
     M, K = A.shape
     N = B.shape[1]
     _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
+    _scales(dev, 1, scale_a=scale_a, scale_b=scale_b)
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
     with _on(A.device):
@@ -285,7 +334,7 @@ def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=No
             _check("fp8_gemm", lib.fp8_gemm(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N, K,
                                             code | flags, _stream(A.device, stream)))
         else:
-            _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous GPU tensor")
+            _arg(workspace, "workspace", dev, (workspace.dtype,))
             _check("fp8_gemm_ws", lib.fp8_gemm_ws(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N,
                                                   K, code | flags, _ptr(workspace),
                                                   workspace.numel() * workspace.element_size(),
@@ -300,10 +349,12 @@ def fp8_gemm_noalloc(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, s
     the library; C is allocated here only when not given).  Calls on one GPU
     must not overlap in time."""
     flags = _fmt_flag(A, a_fmt, FP8_A_E5M2) | _fmt_flag(B, b_fmt, FP8_B_E5M2) | (FP8_ACC_FAST if fast else 0)
+    dev = _operands(A, B)
     A, B = _codes(A), _codes(B)
     M, K = A.shape
     N = B.shape[1]
     _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
+    _scales(dev, 1, scale_a=scale_a, scale_b=scale_b)
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
     with _on(A.device):
@@ -317,10 +368,13 @@ def fp8_gemm_blockscaled(A, B, s_a, s_b, out_dtype=torch.bfloat16, C=None, strea
     (block 32 or 64; E4M3 operands)."""
     _require(block in (32, 64), "block must be 32 or 64")
     _require(_fmt_flag(A, None, 1) == 0 and _fmt_flag(B, None, 1) == 0, "the block-scaled GEMM takes E4M3 operands")
+    dev = _operands(A, B)
     A, B = _codes(A), _codes(B)
     M, K = A.shape
     N = B.shape[1]
     _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
+    _arg(s_a, "s_a", dev, _F32, (M // block) * (K // block), True)
+    _arg(s_b, "s_b", dev, _F32, (K // block) * (N // block), True)
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
     with _on(A.device):
@@ -334,11 +388,14 @@ def fp8_gemm_blockscaled_e8m0(A, B, e_a, e_b, out_dtype=torch.bfloat16, C=None, 
     """C = sum over 32-deep K blocks of 2^(e_a-127) * 2^(e_b-127) * (A_kb @ B_kb) on the FP8 matrix cores
     (32x32 tile exponents, e_a [K/32, pitch(M/32)] and e_b [K/32, pitch(N/32)]; E4M3 operands)."""
     _require(_fmt_flag(A, None, 1) == 0 and _fmt_flag(B, None, 1) == 0, "E4M3 operands only")
-    _require(e_a.dtype == torch.uint8 and e_b.dtype == torch.uint8, "tile exponents must be uint8 tensors")
+    dev = _operands(A, B)
     A, B = _codes(A), _codes(B)
     M, K = A.shape
     N = B.shape[1]
     _require(B.shape[0] == K, "A is %s but B is %s" % (tuple(A.shape), tuple(B.shape)))
+    pitch = lambda n: (n + 3) // 4 * 4
+    _arg(e_a, "e_a", dev, (torch.uint8,), (K // 32) * pitch(M // 32), True)
+    _arg(e_b, "e_b", dev, (torch.uint8,), (K // 32) * pitch(N // 32), True)
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
     with _on(A.device):
@@ -355,10 +412,12 @@ def fp8_quantize_2of4(w: torch.Tensor, vals=None, idx=None, scale=None, amax=Non
              "w must be a contiguous 2-D float32 GPU tensor")
     K, N = w.shape
     dev = w.device
-    vals = torch.empty((K // 2, N), dtype=torch.uint8, device=dev) if vals is None else vals
-    idx = torch.empty((K // 32, N), dtype=torch.int32, device=dev) if idx is None else idx
-    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
-    amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else amax
+    vals = (torch.empty((K // 2, N), dtype=torch.uint8, device=dev) if vals is None
+            else _arg(vals, "vals", dev, _CODES, (K // 2) * N))
+    idx = (torch.empty((K // 32, N), dtype=torch.int32, device=dev) if idx is None
+           else _arg(idx, "idx", dev, (torch.int32,), (K // 32) * N))
+    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else _arg(scale, "scale", dev, _F32, 1, True)
+    amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else _arg(amax, "amax", dev, _F32, 1, True)
     with _on(dev):
         _check("fp8_quantize_2of4", lib.fp8_quantize_2of4(_ptr(w), K, N, _ptr(vals), _ptr(idx), _ptr(scale),
                                                           _ptr(amax), _stream(dev, stream)))
@@ -369,12 +428,15 @@ def fp8_gemm_sparse24(A, vals, idx, scale_a, scale_b, out_dtype=torch.bfloat16, 
     """C = scale_a*scale_b * A @ B with E4M3 A (M x K) and a 2:4-sparse B given compressed
     (vals [K/2, N], idx [K/32, N]) on the sparse FP8 matrix cores."""
     _require(_fmt_flag(A, None, 1) == 0, "E4M3 operands only")
+    dev = _operands(A, vals)
+    _arg(idx, "idx", dev, (torch.int32,))
     A = _codes(A)
     vals = vals.view(torch.uint8) if vals.dtype == torch.float8_e4m3fn else vals
     M, K = A.shape
     N = vals.shape[1]
     _require(vals.shape[0] * 2 == K and tuple(idx.shape) == (K // 32, N), "A is %s but vals %s, idx %s" % (
         tuple(A.shape), tuple(vals.shape), tuple(idx.shape)))
+    _scales(dev, 1, scale_a=scale_a, scale_b=scale_b)
     code = _out_code(out_dtype)
     C = _out_tensor(C, (M, N), code, A.device)
     with _on(A.device):
@@ -388,10 +450,13 @@ def fp8_grouped_gemm(A, B, offsets, scale_a, scale_b, out_dtype=torch.bfloat16, 
                      a_fmt=None, b_fmt=None):
     """MoE grouped GEMM: rows offsets[e]..offsets[e+1] of A times B[e], scaled by scale_a[e]*scale_b[e]."""
     flags = _fmt_flag(A, a_fmt, FP8_A_E5M2) | _fmt_flag(B, b_fmt, FP8_B_E5M2) | (FP8_ACC_FAST if fast else 0)
+    dev = _operands(A, B, 2, 3)
     A, B = _codes(A), _codes(B)
     T, K = A.shape
     E, K2, N = B.shape
+    _arg(offsets, "offsets", dev, (torch.int32,))
     _require(K2 == K and offsets.numel() == E + 1, "shape mismatch")
+    _scales(dev, E, scale_a=scale_a, scale_b=scale_b)
     code = _out_code(out_dtype)
     C = _out_tensor(C, (T, N), code, A.device)
     with _on(A.device):
@@ -406,6 +471,11 @@ def fp8_attention(Q, K, V, scale_q, scale_k, scale_v, softmax_scale=None, causal
     """Multi-head attention on E4M3 codes: Q [BH, Sq, D], K and V [BH, Skv, D] (D = 64 or 128),
     per-tensor scales; softmax_scale defaults to 1/sqrt(D); returns O [BH, Sq, D] of out_dtype.
     fast=True computes Q K^T on the FP8 matrix cores (FP8_ACC_FAST)."""
+    _require(isinstance(Q, torch.Tensor) and Q.is_cuda, "Q must be a GPU tensor")
+    dev = Q.device
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        _arg(t, name, dev, _CODES)
+    _scales(dev, 1, scale_q=scale_q, scale_k=scale_k, scale_v=scale_v)
     Q, K, V = _codes(Q), _codes(K), _codes(V)
     _require(Q.dim() == 3 and K.dim() == 3 and V.dim() == 3, "Q, K, V must be [heads, seq, head_dim]")
     BH, Sq, D = Q.shape
@@ -415,7 +485,7 @@ def fp8_attention(Q, K, V, scale_q, scale_k, scale_v, softmax_scale=None, causal
     if softmax_scale is None:
         softmax_scale = 1.0 / float(D) ** 0.5
     code = _out_code(out_dtype)
-    O = _out_tensor(O, (BH, Sq, D), code, Q.device)
+    O = _out_tensor(O, (BH, Sq, D), code, Q.device, "O")
     with _on(Q.device):
         _check("fp8_attention", lib.fp8_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(scale_q), _ptr(scale_k), _ptr(scale_v),
                                                   _ptr(O), BH, Sq, Skv, D, float(softmax_scale), int(bool(causal)),

@@ -259,3 +259,38 @@ def test_attention_validation(kw, status):
     assert attention(**kw) == status
     if status != P.FP8_OK:
         assert P.lib.fp8_last_error().decode() != ""
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    """Host (CPU) tensors never reach the library: every entry point of the
+    binding raises before its first HIP call, since a host pointer handed to
+    a kernel would fault the GPU."""
+    import torch
+    x = torch.zeros(64, 64)
+    c = torch.zeros(64, 64, dtype=torch.uint8)
+    b3 = torch.zeros(2, 64, 64, dtype=torch.uint8)
+    s = torch.ones(1)
+    off = torch.tensor([0, 32, 64], dtype=torch.int32)
+    calls = {
+        "fp8_quantize": lambda: P.fp8_quantize(x),
+        "fp8_quantize_e5m2": lambda: P.fp8_quantize_e5m2(x),
+        "fp8_quantize_blocked": lambda: P.fp8_quantize_blocked(x),
+        "fp8_quantize_blocked64": lambda: P.fp8_quantize_blocked64(x),
+        "fp8_quantize_blocked_e8m0": lambda: P.fp8_quantize_blocked_e8m0(x),
+        "fp8_quantize_grouped": lambda: P.fp8_quantize_grouped(x, off),
+        "fp8_quantize_grouped_e5m2": lambda: P.fp8_quantize_grouped_e5m2(x, off),
+        "fp8_quantize_2of4": lambda: P.fp8_quantize_2of4(x),
+        "fp8_gemm": lambda: P.fp8_gemm(c, c, s, s),
+        "fp8_gemm_ws": lambda: P.fp8_gemm(c, c, s, s, workspace=torch.zeros(16, dtype=torch.uint8)),
+        "fp8_gemm_noalloc": lambda: P.fp8_gemm_noalloc(c, c, s, s),
+        "fp8_gemm_blockscaled": lambda: P.fp8_gemm_blockscaled(c, c, torch.ones(2, 2), torch.ones(2, 2)),
+        "fp8_gemm_blockscaled_e8m0": lambda: P.fp8_gemm_blockscaled_e8m0(c, c, torch.zeros(2, 4, dtype=torch.uint8),
+                                                                         torch.zeros(2, 4, dtype=torch.uint8)),
+        "fp8_gemm_sparse24": lambda: P.fp8_gemm_sparse24(c, torch.zeros(32, 64, dtype=torch.uint8),
+                                                         torch.zeros(2, 64, dtype=torch.int32), s, s),
+        "fp8_grouped_gemm": lambda: P.fp8_grouped_gemm(c, b3, off, torch.ones(2), torch.ones(2)),
+        "fp8_attention": lambda: P.fp8_attention(b3, b3, b3, s, s, s),
+    }
+    for name, call in calls.items():
+        with pytest.raises(ValueError, match="GPU tensor"):
+            call()

@@ -334,7 +334,7 @@ def fp8_gemm(A, B, scale_a, scale_b, out_dtype=torch.bfloat16, C=None, stream=No
             _check("fp8_gemm", lib.fp8_gemm(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N, K,
                                             code | flags, _stream(A.device, stream)))
         else:
-            _arg(workspace, "workspace", dev, (workspace.dtype,))
+            _arg(workspace, "workspace", dev, (getattr(workspace, "dtype", None),))
             _check("fp8_gemm_ws", lib.fp8_gemm_ws(_ptr(A), _ptr(B), _ptr(scale_a), _ptr(scale_b), _ptr(C), M, N,
                                                   K, code | flags, _ptr(workspace),
                                                   workspace.numel() * workspace.element_size(),
